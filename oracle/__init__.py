@@ -1,0 +1,168 @@
+"""Python front of the float64 reference oracle (oracle.c).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg are the only callers.  The GPU library never imports this
+package and this package never imports the GPU library; the two share nothing
+but the seeded inputs of the `workload` module.
+
+Each function converts its inputs exactly to float64 (bf16 bit patterns or
+float32 both widen without rounding) and calls the C definition.  Citations
+for every definition are in oracle.c.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+BUILD_CMD = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-o", _LIB, _SRC, "-lm", "-lpthread"]
+
+_lib = None
+
+
+def build() -> str:
+    subprocess.run(BUILD_CMD, check=True)
+    return _LIB
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        L = ctypes.CDLL(_LIB)
+        dp = ctypes.POINTER(ctypes.c_double)
+        ip = ctypes.POINTER(ctypes.c_int32)
+        lp = ctypes.POINTER(ctypes.c_int64)
+        L.oracle_rope_freq.argtypes = [ctypes.c_double, ctypes.c_int, ctypes.c_int]
+        L.oracle_rope_freq.restype = ctypes.c_double
+        L.oracle_rope.argtypes = [dp, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ip, ctypes.c_double]
+        L.oracle_rope.restype = None
+        L.oracle_attention.argtypes = [dp, dp, dp, dp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_int64, ctypes.c_int64, ctypes.c_double, lp, ctypes.c_int64,
+                                       ctypes.c_int]
+        L.oracle_attention.restype = ctypes.c_int
+        L.oracle_descriptor_count.argtypes = [ctypes.c_int] * 5
+        L.oracle_descriptor_count.restype = ctypes.c_int
+        L.oracle_descriptor_pool.argtypes = [dp, dp] + [ctypes.c_int] * 9
+        L.oracle_descriptor_pool.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def default_threads() -> int:
+    n = os.cpu_count() or 1
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return n
+
+
+def _dp(a: np.ndarray):
+    assert a.dtype == np.float64 and a.flags.c_contiguous
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def to_f64(x: np.ndarray) -> np.ndarray:
+    """Exact widening: uint16 arrays are bf16 bit patterns; float32/float64 as is."""
+    if x.dtype == np.uint16:
+        return (x.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    return np.ascontiguousarray(x, dtype=np.float64)
+
+
+def rope_freq(base: float, d_axis: int, k: int) -> float:
+    return lib().oracle_rope_freq(base, d_axis, k)
+
+
+def rope(x: np.ndarray, pos_tok: np.ndarray, base: float) -> np.ndarray:
+    """Rotated copy of x [n_tok, H, D] (float64) for per-token positions
+    pos_tok [n_tok, 2] (row, col)."""
+    y = np.array(to_f64(x), dtype=np.float64, order="C", copy=True)
+    n_tok, H, D = y.shape
+    p = np.ascontiguousarray(pos_tok, dtype=np.int32).reshape(n_tok, 2)
+    lib().oracle_rope(_dp(y), n_tok, H, D, p.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), float(base))
+    return y
+
+
+def attention(q, k, v, *, group_q: int = 0, group_k: int = 0, scale: float | None = None, rows=None,
+              nthreads: int | None = None) -> np.ndarray:
+    """Multi-head softmax attention.  q [nq, H, D], k/v [nk, H, D] (any of
+    bf16-bits/float32/float64).  Returns float64 [len(rows) or nq, H, D]."""
+    q64, k64, v64 = to_f64(q), to_f64(k), to_f64(v)
+    nq, H, D = q64.shape
+    nk = k64.shape[0]
+    assert k64.shape == (nk, H, D) and v64.shape == (nk, H, D)
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    if rows is None:
+        r = None
+        nrows = nq
+        rp = None
+    else:
+        r = np.ascontiguousarray(rows, dtype=np.int64)
+        nrows = r.size
+        rp = r.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    o = np.zeros((nrows, H, D), dtype=np.float64)
+    rc = lib().oracle_attention(_dp(q64), _dp(k64), _dp(v64), _dp(o), nq, nk, H, D, group_q, group_k, float(scale),
+                                rp, nrows, nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_attention: bad arguments")
+    return o
+
+
+def _frame_positions(pos: np.ndarray, S: int) -> np.ndarray:
+    return np.tile(np.asarray(pos, dtype=np.int32).reshape(-1, 2), (S, 1))
+
+
+def frame_attn(q, k, v, S: int, T: int, pos=None, base: float = 100.0, scale=None, rows=None, nthreads=None):
+    """Frame-wise attention: S independent sequences of T tokens.
+    q/k/v [S, T, H, D]; pos [T, 2] shared by all frames (None: no RoPE).
+    rows index tokens of the flattened [S*T] axis."""
+    H, D = q.shape[-2:]
+    qf, kf, vf = (to_f64(x).reshape(S * T, H, D) for x in (q, k, v))
+    if pos is not None:
+        pt = _frame_positions(pos, S)
+        qf, kf = rope(qf, pt, base), rope(kf, pt, base)
+    return attention(qf, kf, vf, group_q=T, group_k=T, scale=scale, rows=rows, nthreads=nthreads)
+
+
+def global_attn(q, k, v, S: int, T: int, pos=None, base: float = 100.0, scale=None, rows=None, nthreads=None):
+    """Global attention: one sequence of S*T tokens; each token keeps its own
+    within-frame (row, col) position for RoPE."""
+    H, D = q.shape[-2:]
+    qf, kf, vf = (to_f64(x).reshape(S * T, H, D) for x in (q, k, v))
+    if pos is not None:
+        pt = _frame_positions(pos, S)
+        qf, kf = rope(qf, pt, base), rope(kf, pt, base)
+    return attention(qf, kf, vf, scale=scale, rows=rows, nthreads=nthreads)
+
+
+def descriptor_count(T: int, gh: int, gw: int, ph: int, pw: int) -> int:
+    return lib().oracle_descriptor_count(T, gh, gw, ph, pw)
+
+
+def descriptor_pool(x, S: int, T: int, gh: int, gw: int, patch_begin: int, ph: int, pw: int) -> np.ndarray:
+    """x [S, T, H, D] -> float64 [S, Dn, H, D]."""
+    H, D = x.shape[-2:]
+    x64 = to_f64(x).reshape(S, T, H, D)
+    Dn = descriptor_count(T, gh, gw, ph, pw)
+    out = np.zeros((S, Dn, H, D), dtype=np.float64)
+    rc = lib().oracle_descriptor_pool(_dp(x64), _dp(out), S, T, H, D, gh, gw, patch_begin, ph, pw)
+    if rc != 0:
+        raise ValueError("oracle_descriptor_pool: bad arguments")
+    return out
+
+
+def descriptor_xattn(q, kd, vd, scale=None, rows=None, nthreads=None) -> np.ndarray:
+    """Every query token [S, T, H, D] attends to every descriptor [S, Dn, H, D]."""
+    H, D = q.shape[-2:]
+    qf = to_f64(q).reshape(-1, H, D)
+    kf = to_f64(kd).reshape(-1, H, D)
+    vf = to_f64(vd).reshape(-1, H, D)
+    return attention(qf, kf, vf, scale=scale, rows=rows, nthreads=nthreads)

@@ -1,0 +1,375 @@
+"""Pins of the float64 oracle against facts fixed outside the oracle itself:
+values printed on the pages (tests/golden), closed forms, invariants,
+library routines and brute force on tiny inputs.  CPU only."""
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+
+import oracle
+import workload
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _load(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name), encoding="utf-8") as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append([float(x) for x in line.split()])
+    return np.array(rows)
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# --------------------------------------------------------------------------
+# Printed worked examples
+# --------------------------------------------------------------------------
+
+def test_softmax_matches_printed_slide_example():
+    """Slide deck Section V 4/10: scores (2, 1, 0.5, -1) -> (0.61, 0.22, 0.14, 0.03).
+    With V = one-hot rows the attention output of one query is the softmax
+    vector itself; D = 4 gives scale 1/2, so q = 4 e0 and k_j0 = s_j / 2."""
+    g = _load("softmax_slide.txt")
+    scores, printed = g[:, 0], g[:, 1]
+    D = 4
+    q = np.zeros((1, 1, D)); q[0, 0, 0] = 4.0
+    k = np.zeros((4, 1, D)); k[:, 0, 0] = scores / 2.0
+    v = np.eye(4).reshape(4, 1, D)
+    o = oracle.attention(q, k, v)[0, 0]
+    assert np.all(np.abs(o - printed) <= 0.005 + 1e-12)
+    assert abs(o.sum() - 1.0) < 1e-15
+    # and the exact values against the closed form e^s / sum e^s
+    np.testing.assert_allclose(o, np.exp(scores) / np.exp(scores).sum(), rtol=1e-15)
+
+
+def test_rope_frequency_table_matches_printed_sinusoid_slide():
+    """Slide deck Section IV 6/6 prints the first values of the base-10000
+    sinusoidal encoding at pos 1..3.  The oracle's RoPE rotates pair (0,1) of
+    an axis by pos*freq(k=0) and pair (2,3) by pos*freq(k=1); with d_axis = 4
+    and base 10000, rotating the unit vectors e0 and e2 must reproduce
+    (sin, cos, sin, cos) of the printed table.  Checked on both axes."""
+    g = _load("sinusoid_slide.txt")
+    D = 8  # two axes of width 4
+    for axis in (0, 1):
+        for row in g:
+            p = int(row[0])
+            pos = np.zeros((2, 2), dtype=np.int32)
+            pos[:, axis] = p
+            x = np.zeros((2, 1, D))
+            x[0, 0, 4 * axis + 0] = 1.0   # e0 of this axis
+            x[1, 0, 4 * axis + 2] = 1.0   # e2 of this axis
+            y = oracle.rope(x, pos, 10000.0)
+            c0, s0 = y[0, 0, 4 * axis + 0], y[0, 0, 4 * axis + 1]
+            c1, s1 = y[1, 0, 4 * axis + 2], y[1, 0, 4 * axis + 3]
+            got = np.array([s0, c0, s1, c1])
+            assert np.all(np.abs(got - row[1:]) <= 0.005 + 1e-12), (axis, p, got, row)
+            # the other axis is untouched
+            other = [i for i in range(D) if i // 4 != axis]
+            assert np.all(y[:, 0, other] == 0.0)
+    assert oracle.rope_freq(10000.0, 4, 1) == pytest.approx(0.01, rel=1e-15)
+    assert oracle.rope_freq(100.0, 32, 0) == 1.0
+
+
+# --------------------------------------------------------------------------
+# RoPE closed forms
+# --------------------------------------------------------------------------
+
+def test_rope_identity_at_origin_is_bitwise():
+    x = workload.normal_f32(11, (7, 3, 64)).astype(np.float64)
+    y = oracle.rope(x, np.zeros((7, 2), np.int32), 100.0)
+    assert np.array_equal(x, y)
+
+
+def test_rope_preserves_norm_and_rotates_pairs():
+    r = _rng(1)
+    x = r.standard_normal((50, 2, 64))
+    pos = r.integers(0, 40, size=(50, 2)).astype(np.int32)
+    y = oracle.rope(x, pos, 100.0)
+    np.testing.assert_allclose(np.linalg.norm(y, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-13)
+    # each pair keeps its own norm (a rotation of that pair only)
+    np.testing.assert_allclose(np.hypot(y[..., 0::2], y[..., 1::2]), np.hypot(x[..., 0::2], x[..., 1::2]),
+                               rtol=1e-12, atol=1e-14)
+    # explicit angle of one pair: dims (32+2k, 33+2k) rotate by col * 100^(-2k/32)
+    t, h, k = 3, 1, 5
+    theta = pos[t, 1] * 100.0 ** (-2 * k / 32)
+    a, b = x[t, h, 32 + 2 * k], x[t, h, 33 + 2 * k]
+    assert y[t, h, 32 + 2 * k] == pytest.approx(a * math.cos(theta) - b * math.sin(theta), abs=1e-13)
+    assert y[t, h, 33 + 2 * k] == pytest.approx(a * math.sin(theta) + b * math.cos(theta), abs=1e-13)
+
+
+def test_rope_relative_position_property():
+    """<rope(q, p), rope(k, p')> = <rope(q, p - p'), k> for every head vector."""
+    r = _rng(2)
+    q = r.standard_normal((20, 1, 64))
+    k = r.standard_normal((20, 1, 64))
+    p = r.integers(-30, 30, size=(20, 2)).astype(np.int32)
+    pp = r.integers(-30, 30, size=(20, 2)).astype(np.int32)
+    lhs = np.sum(oracle.rope(q, p, 100.0) * oracle.rope(k, pp, 100.0), axis=-1)
+    rhs = np.sum(oracle.rope(q, (p - pp).astype(np.int32), 100.0) * k, axis=-1)
+    np.testing.assert_allclose(lhs, rhs, rtol=1e-11, atol=1e-11)
+
+
+def test_attention_invariant_under_common_position_shift():
+    """Shifting every token's (row, col) by one constant leaves attention
+    unchanged (scores depend on position differences only)."""
+    wl = workload.Workload("t", 9, S=2, gh=3, gw=4, n_special=2, patch_begin=2, H=2, D=64)
+    q, k, v = wl.qkv_f32()
+    pos = wl.positions()
+    a = oracle.global_attn(q, k, v, wl.S, wl.T, pos=pos)
+    b = oracle.global_attn(q, k, v, wl.S, wl.T, pos=(pos + np.array([7, -3], np.int32)).astype(np.int32))
+    np.testing.assert_allclose(a, b, rtol=1e-11, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# Attention closed forms
+# --------------------------------------------------------------------------
+
+def test_identical_keys_average_values():
+    r = _rng(3)
+    q = r.standard_normal((5, 2, 64))
+    k = np.repeat(r.standard_normal((1, 2, 64)), 9, axis=0)
+    v = r.standard_normal((9, 2, 64))
+    o = oracle.attention(q, k, v)
+    np.testing.assert_allclose(o, np.broadcast_to(v.mean(axis=0), o.shape), rtol=1e-13, atol=1e-15)
+
+
+def test_dominant_key_selects_its_value():
+    r = _rng(4)
+    D = 64
+    q = np.zeros((1, 1, D)); q[0, 0, 0] = 1.0
+    k = r.standard_normal((12, 1, D)) * 0.01
+    k[7, 0, 0] = 8.0 * 60.0      # score margin >= 50 after the 1/8 scale
+    v = r.standard_normal((12, 1, D))
+    o = oracle.attention(q, k, v)
+    np.testing.assert_allclose(o[0, 0], v[7, 0], rtol=0, atol=12 * math.exp(-50) * 10)
+
+
+def test_single_key_and_constant_values():
+    r = _rng(5)
+    q = r.standard_normal((4, 3, 64))
+    k1 = r.standard_normal((1, 3, 64))
+    v1 = r.standard_normal((1, 3, 64))
+    np.testing.assert_allclose(oracle.attention(q, k1, v1), np.broadcast_to(v1, (4, 3, 64)), rtol=1e-15)
+    k = r.standard_normal((10, 3, 64))
+    v = np.full((10, 3, 64), 0.3125)
+    np.testing.assert_allclose(oracle.attention(q, k, v), 0.3125, rtol=1e-14)
+
+
+def test_softmax_against_library_routine():
+    """With V = identity rows (nk = D) the output row is softmax(scale q K^T),
+    computed here by scipy.special.softmax."""
+    r = _rng(6)
+    D = 16
+    q = r.standard_normal((6, 2, D)) * 3
+    k = r.standard_normal((D, 2, D))
+    v = np.repeat(np.eye(D)[:, None, :], 2, axis=1)
+    o = oracle.attention(q, k, v, scale=0.37)
+    for h in range(2):
+        ref = scipy.special.softmax(0.37 * q[:, h, :] @ k[:, h, :].T, axis=-1)
+        np.testing.assert_allclose(o[:, h, :], ref, rtol=1e-13, atol=1e-16)
+
+
+def test_key_shift_invariance():
+    """K -> K + 1 c^T changes every score of a row by the same q.c."""
+    r = _rng(7)
+    q = r.standard_normal((8, 2, 64))
+    k = r.standard_normal((30, 2, 64))
+    v = r.standard_normal((30, 2, 64))
+    c = r.standard_normal((1, 2, 64))
+    np.testing.assert_allclose(oracle.attention(q, k, v), oracle.attention(q, k + c, v), rtol=1e-11, atol=1e-13)
+
+
+def test_linearity_in_values():
+    r = _rng(8)
+    q = r.standard_normal((8, 1, 64))
+    k = r.standard_normal((30, 1, 64))
+    v = r.standard_normal((30, 1, 64))
+    A = r.standard_normal((64, 64))
+    b = r.standard_normal(64)
+    lhs = oracle.attention(q, k, (v[:, 0] @ A + b)[:, None, :])
+    rhs = oracle.attention(q, k, v)[:, 0] @ A + b
+    np.testing.assert_allclose(lhs[:, 0], rhs, rtol=1e-10, atol=1e-11)
+
+
+def test_heads_are_independent():
+    r = _rng(9)
+    q = r.standard_normal((6, 3, 64))
+    k = r.standard_normal((11, 3, 64))
+    v = r.standard_normal((11, 3, 64))
+    o = oracle.attention(q, k, v)
+    for h in range(3):
+        oh = oracle.attention(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1])
+        np.testing.assert_array_equal(o[:, h:h + 1], oh)
+
+
+def test_token_and_kv_permutation():
+    """Global attention without RoPE: permuting queries permutes outputs;
+    permuting keys and values together changes nothing."""
+    r = _rng(10)
+    q = r.standard_normal((13, 2, 64))
+    k = r.standard_normal((17, 2, 64))
+    v = r.standard_normal((17, 2, 64))
+    o = oracle.attention(q, k, v)
+    pq = r.permutation(13)
+    pk = r.permutation(17)
+    np.testing.assert_allclose(oracle.attention(q[pq], k, v), o[pq], rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(oracle.attention(q, k[pk], v[pk]), o, rtol=1e-12, atol=1e-14)
+
+
+def test_frame_permutation_equivariance_with_rope():
+    """Positions are within-frame only, so permuting whole frames permutes
+    the outputs of both frame and global attention, RoPE on."""
+    wl = workload.Workload("t", 8, S=3, gh=3, gw=4, n_special=2, patch_begin=2, H=2, D=64)
+    q, k, v = wl.qkv_f32()
+    pos = wl.positions()
+    perm = np.array([2, 0, 1])
+    for fn in (oracle.frame_attn, oracle.global_attn):
+        o = fn(q, k, v, wl.S, wl.T, pos=pos).reshape(wl.S, wl.T, 2, 64)
+        op = fn(q[perm], k[perm], v[perm], wl.S, wl.T, pos=pos).reshape(wl.S, wl.T, 2, 64)
+        np.testing.assert_allclose(op, o[perm], rtol=1e-12, atol=1e-14)
+
+
+def _einsum_attention(q, k, v, scale):
+    # brute force on tiny inputs: full score tensor, library exp/sum
+    s = np.einsum("qhd,khd->hqk", q, k) * scale
+    p = np.exp(s - s.max(axis=-1, keepdims=True))
+    p /= p.sum(axis=-1, keepdims=True)
+    return np.einsum("hqk,khd->qhd", p, v)
+
+
+def _einsum_rope(x, pos, base):
+    # rotation written as a complex multiply per (2k, 2k+1) pair
+    n, H, D = x.shape
+    half = D // 2
+    out = np.empty_like(x)
+    for a in range(2):
+        z = x[..., a * half:(a + 1) * half:2] + 1j * x[..., a * half + 1:(a + 1) * half:2]
+        freqs = base ** (-2.0 * np.arange(half // 2) / half)
+        rot = np.exp(1j * pos[:, a, None].astype(np.float64) * freqs[None, :])
+        z = z * rot[:, None, :]
+        out[..., a * half:(a + 1) * half:2] = z.real
+        out[..., a * half + 1:(a + 1) * half:2] = z.imag
+    return out
+
+
+@pytest.mark.parametrize("S,H", [(1, 1), (2, 2), (3, 2)])
+def test_brute_force_tiny(S, H):
+    wl = workload.Workload("t", 7, S=S, gh=3, gw=4, n_special=2, patch_begin=2, H=H, D=64)
+    q, k, v = (x.astype(np.float64) for x in wl.qkv_f32())
+    pos = wl.positions()
+    T = wl.T
+    pt = np.tile(pos, (S, 1))
+    qr = _einsum_rope(q.reshape(S * T, H, 64), pt, 100.0)
+    kr = _einsum_rope(k.reshape(S * T, H, 64), pt, 100.0)
+    vv = v.reshape(S * T, H, 64)
+    g_ref = _einsum_attention(qr, kr, vv, 0.125)
+    np.testing.assert_allclose(oracle.global_attn(q, k, v, S, T, pos=pos), g_ref, rtol=1e-11, atol=1e-13)
+    f_ref = np.concatenate([_einsum_attention(qr[s * T:(s + 1) * T], kr[s * T:(s + 1) * T], vv[s * T:(s + 1) * T],
+                                              0.125) for s in range(S)])
+    np.testing.assert_allclose(oracle.frame_attn(q, k, v, S, T, pos=pos), f_ref, rtol=1e-11, atol=1e-13)
+
+
+def test_frame_vs_global_consistency_and_row_sampling():
+    wl = workload.Workload("t", 6, S=3, gh=4, gw=4, n_special=5, patch_begin=5, H=2, D=64)
+    q, k, v = wl.qkv_bf16()
+    pos = wl.positions()
+    T = wl.T
+    f = oracle.frame_attn(q, k, v, wl.S, T, pos=pos)
+    for s in range(wl.S):
+        g1 = oracle.global_attn(q[s:s + 1], k[s:s + 1], v[s:s + 1], 1, T, pos=pos)
+        np.testing.assert_array_equal(f[s * T:(s + 1) * T], g1)
+    rows = np.array([0, 4, T, 2 * T + 3, 3 * T - 1])
+    np.testing.assert_array_equal(oracle.frame_attn(q, k, v, wl.S, T, pos=pos, rows=rows), f[rows])
+    g = oracle.global_attn(q, k, v, wl.S, T, pos=pos)
+    np.testing.assert_array_equal(oracle.global_attn(q, k, v, wl.S, T, pos=pos, rows=rows), g[rows])
+
+
+# --------------------------------------------------------------------------
+# Descriptor pooling and cross-attention
+# --------------------------------------------------------------------------
+
+def _brute_pool(x, gh, gw, pb, ph, pw):
+    S, T, H, D = x.shape
+    spec = [t for t in range(T) if not (pb <= t < pb + gh * gw)]
+    out = []
+    for s in range(S):
+        toks = [x[s, t] for t in spec]
+        grid = x[s, pb:pb + gh * gw].reshape(gh, gw, H, D)
+        for a in range(0, gh, ph):
+            for b in range(0, gw, pw):
+                toks.append(grid[a:a + ph, b:b + pw].reshape(-1, H, D).mean(axis=0))
+        out.append(np.stack(toks))
+    return np.stack(out)
+
+
+def test_descriptor_count():
+    assert oracle.descriptor_count(1374, 37, 37, 2, 2) == 366
+    assert oracle.descriptor_count(1040, 32, 32, 2, 2) == 16 + 256
+    assert oracle.descriptor_count(261, 16, 16, 1, 1) == 261
+
+
+@pytest.mark.parametrize("gh,gw,pb,ns,ph,pw", [(5, 7, 3, 3, 2, 2), (4, 4, 0, 2, 2, 2), (3, 5, 1, 1, 3, 2),
+                                               (6, 6, 2, 2, 1, 1)])
+def test_pool_brute_force(gh, gw, pb, ns, ph, pw):
+    r = _rng(gh * 100 + gw)
+    T = gh * gw + ns
+    x = r.standard_normal((2, T, 2, 8))
+    got = oracle.descriptor_pool(x, 2, T, gh, gw, pb, ph, pw)
+    np.testing.assert_allclose(got, _brute_pool(x, gh, gw, pb, ph, pw), rtol=1e-14, atol=1e-15)
+    if ph == pw == 1:
+        # identity up to moving the specials in front
+        spec = [t for t in range(T) if not (pb <= t < pb + gh * gw)]
+        order = spec + list(range(pb, pb + gh * gw))
+        np.testing.assert_array_equal(got, x[:, order])
+
+
+def test_pool_constant_and_ceil_edges():
+    S, gh, gw, pb = 1, 37, 37, 5
+    T = gh * gw + 5
+    x = np.full((S, T, 1, 4), 2.5)
+    np.testing.assert_array_equal(oracle.descriptor_pool(x, S, T, gh, gw, pb, 2, 2), 2.5)
+    r = _rng(12)
+    x = r.standard_normal((S, T, 1, 4))
+    out = oracle.descriptor_pool(x, S, T, gh, gw, pb, 2, 2)
+    grid = x[0, pb:pb + gh * gw].reshape(gh, gw, 1, 4)
+    # corner cell (18, 18) covers only grid cell (36, 36)
+    np.testing.assert_array_equal(out[0, 5 + 18 * 19 + 18], grid[36, 36])
+    # last-column cell (0, 18) averages the two cells (0,36), (1,36)
+    np.testing.assert_allclose(out[0, 5 + 18], (grid[0, 36] + grid[1, 36]) / 2, rtol=1e-15)
+    # an interior cell averages four
+    np.testing.assert_allclose(out[0, 5 + 19 + 1], grid[2:4, 2:4].mean(axis=(0, 1)), rtol=1e-15)
+    # specials come first, unchanged
+    np.testing.assert_array_equal(out[0, :5], x[0, :5])
+
+
+def test_xattn_with_unit_window_equals_global_attention():
+    wl = workload.Workload("t", 5, S=2, gh=3, gw=3, n_special=2, patch_begin=2, H=2, D=64)
+    q, k, v = wl.qkv_bf16()
+    T = wl.T
+    kd = oracle.descriptor_pool(k, wl.S, T, 3, 3, 2, 1, 1)
+    vd = oracle.descriptor_pool(v, wl.S, T, 3, 3, 2, 1, 1)
+    # same key set up to a permutation inside each frame
+    np.testing.assert_allclose(oracle.descriptor_xattn(q, kd, vd), oracle.global_attn(q, k, v, wl.S, T),
+                               rtol=1e-12, atol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# Input generator
+# --------------------------------------------------------------------------
+
+def test_splitmix64_reference_outputs_and_normals():
+    # first outputs of SplitMix64 seeded with 0 (published reference stream)
+    assert [int(x) for x in workload.splitmix64(0, 0, 2)] == [0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4]
+    z = workload.normal_f64(123, 400001)
+    assert abs(z.mean()) < 0.01 and abs(z.var() - 1) < 0.01
+    assert np.array_equal(z[:1001], workload.normal_f64(123, 1001))
+    b = workload.f32_to_bf16_bits(np.array([1.0, 1.00390625, 1.01171875, -2.0, 3.0e-3], np.float32))
+    # 1+2^-8 is a tie -> even (1.0); 1+3*2^-8 is a tie -> up to 1+2^-6
+    np.testing.assert_array_equal(workload.bf16_bits_to_f32(b)[:4], [1.0, 1.0, 1.015625, -2.0])
