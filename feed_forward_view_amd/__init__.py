@@ -1,0 +1,216 @@
+"""Python binding of libvggt_attn (MI355X / gfx950 alternating attention).
+
+Thin argument marshalling over the C ABI declared in include/vggt_attn.h:
+every function checks dtype, shape, contiguity and device of torch tensors,
+passes raw device pointers and the current HIP stream, and raises on a
+non-OK status.  All computation happens in the library's HIP kernels; torch
+only provides device memory and streams.  There is no fallback: if the
+library is missing or fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libvggt_attn.so")
+
+BF16, F32 = 0, 1
+HEAD_DIM = 64
+
+STATUS = {
+    0: "VGGT_OK", 1: "VGGT_ERR_NULL", 2: "VGGT_ERR_SHAPE", 3: "VGGT_ERR_UNSUPPORTED", 4: "VGGT_ERR_ALIGN",
+    5: "VGGT_ERR_ALIAS", 6: "VGGT_ERR_WORKSPACE", 7: "VGGT_ERR_DEVICE",
+}
+
+# name -> (restype, argtypes); pointers are passed as c_void_p
+_vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+SIGNATURES = {
+    "vggt_abi_version": (_i, []),
+    "vggt_status_str": (ctypes.c_char_p, [_i]),
+    "vggt_last_error": (ctypes.c_char_p, []),
+    "vggt_attn_rope": (_i, [_vp, _i, _i, _i, _i, _vp, _f, _vp]),
+    "vggt_frame_attn_workspace": (_sz, [_i, _i, _i, _i, _i]),
+    "vggt_frame_attn": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _f, _f, _vp, _sz, _vp]),
+    "vggt_global_attn_workspace": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "vggt_global_attn": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _f, _f, _i, _vp, _sz, _vp]),
+    "vggt_descriptor_count": (_i, [_i, _i, _i, _i, _i]),
+    "vggt_descriptor_pool": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i, _vp]),
+    "vggt_descriptor_xattn_workspace": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "vggt_descriptor_xattn": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]),
+}
+
+_lib = None
+
+
+class VggtError(RuntimeError):
+    def __init__(self, fn: str, status: int, detail: str):
+        super().__init__(f"{fn} -> {STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load the built library (raises if it is missing)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run python -m feed_forward_view_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise VggtError(fn, status, lib().vggt_last_error().decode(errors="replace"))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
+
+
+def _tok(t: torch.Tensor, name: str) -> tuple[int, int, int]:
+    if t.dim() != 4 or t.shape[-1] != HEAD_DIM:
+        raise ValueError(f"{name} must be [S, T, H, {HEAD_DIM}], got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    return int(t.shape[0]), int(t.shape[1]), int(t.shape[2])
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _pos(pos_yx, T: int):
+    if pos_yx is None:
+        return None
+    if pos_yx.dtype != torch.int32 or tuple(pos_yx.shape) != (T, 2) or not pos_yx.is_contiguous():
+        raise ValueError(f"pos_yx must be contiguous int32 [{T}, 2]")
+    return ctypes.c_void_p(pos_yx.data_ptr())
+
+
+def _workspace(nbytes: int, device, workspace):
+    if nbytes == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"workspace needs {nbytes} bytes")
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+# ---------------------------------------------------------------------------
+# the five calls (names as in the C ABI)
+# ---------------------------------------------------------------------------
+
+def vggt_attn_rope(x: torch.Tensor, pos_yx: torch.Tensor, rope_base: float = 100.0, stream=None) -> torch.Tensor:
+    """Rotate x [S, T, H, 64] in place by 2D RoPE; returns x."""
+    S, T, H = _tok(x, "x")
+    _check("vggt_attn_rope",
+           lib().vggt_attn_rope(_ptr(x), _dtype_code(x), S, T, H, _pos(pos_yx, T), rope_base, _stream(stream)))
+    return x
+
+
+def vggt_frame_attn_workspace(S, T, H, rope_on, dtype=torch.bfloat16) -> int:
+    return int(lib().vggt_frame_attn_workspace(S, T, H, int(bool(rope_on)), BF16 if dtype == torch.bfloat16 else F32))
+
+
+def vggt_frame_attn(q, k, v, out=None, pos_yx=None, rope_base=100.0, scale=0.0, workspace=None, stream=None):
+    """Frame-wise attention over [S, T, H, 64]; returns out."""
+    S, T, H = _tok(q, "q")
+    for n, t in (("k", k), ("v", v)):
+        if _tok(t, n) != (S, T, H) or t.dtype != q.dtype:
+            raise ValueError(f"{n} must match q")
+    out = torch.empty_like(q) if out is None else out
+    if _tok(out, "out") != (S, T, H) or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    need = vggt_frame_attn_workspace(S, T, H, pos_yx is not None, q.dtype)
+    ws, nbytes = _workspace(need, q.device, workspace)
+    _check("vggt_frame_attn",
+           lib().vggt_frame_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _dtype_code(q), S, T, H, _pos(pos_yx, T),
+                                 rope_base, scale, _ptr(ws), nbytes, _stream(stream)))
+    return out
+
+
+def vggt_global_attn_workspace(S, T, H, kv_splits, rope_on, dtype=torch.bfloat16) -> int:
+    return int(lib().vggt_global_attn_workspace(S, T, H, kv_splits, int(bool(rope_on)),
+                                                BF16 if dtype == torch.bfloat16 else F32))
+
+
+def vggt_global_attn(q, k, v, out=None, pos_yx=None, rope_base=100.0, scale=0.0, kv_splits=0, workspace=None,
+                     stream=None):
+    """Global attention over all S*T tokens; returns out."""
+    S, T, H = _tok(q, "q")
+    for n, t in (("k", k), ("v", v)):
+        if _tok(t, n) != (S, T, H) or t.dtype != q.dtype:
+            raise ValueError(f"{n} must match q")
+    out = torch.empty_like(q) if out is None else out
+    if _tok(out, "out") != (S, T, H) or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    need = vggt_global_attn_workspace(S, T, H, kv_splits, pos_yx is not None, q.dtype)
+    ws, nbytes = _workspace(need, q.device, workspace)
+    _check("vggt_global_attn",
+           lib().vggt_global_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _dtype_code(q), S, T, H, _pos(pos_yx, T),
+                                  rope_base, scale, kv_splits, _ptr(ws), nbytes, _stream(stream)))
+    return out
+
+
+def vggt_descriptor_count(T, gh, gw, ph, pw) -> int:
+    return int(lib().vggt_descriptor_count(T, gh, gw, ph, pw))
+
+
+def vggt_descriptor_pool(k, v, gh, gw, patch_begin, ph=2, pw=2, kd=None, vd=None, stream=None):
+    """Pool K and V [S, T, H, 64] into descriptors [S, Dn, H, 64]; returns (kd, vd)."""
+    S, T, H = _tok(k, "k")
+    if _tok(v, "v") != (S, T, H) or v.dtype != k.dtype:
+        raise ValueError("v must match k")
+    Dn = vggt_descriptor_count(T, gh, gw, ph, pw)
+    if Dn < 1:
+        raise ValueError("bad pooling grid")
+    kd = torch.empty((S, Dn, H, HEAD_DIM), dtype=k.dtype, device=k.device) if kd is None else kd
+    vd = torch.empty((S, Dn, H, HEAD_DIM), dtype=k.dtype, device=k.device) if vd is None else vd
+    for n, t in (("kd", kd), ("vd", vd)):
+        if _tok(t, n) != (S, Dn, H) or t.dtype != k.dtype:
+            raise ValueError(f"{n} must be [{S}, {Dn}, {H}, 64]")
+    _check("vggt_descriptor_pool",
+           lib().vggt_descriptor_pool(_ptr(k), _ptr(v), _ptr(kd), _ptr(vd), _dtype_code(k), S, T, H, gh, gw,
+                                      patch_begin, ph, pw, _stream(stream)))
+    return kd, vd
+
+
+def vggt_descriptor_xattn_workspace(S, T, Dn, H, kv_splits, dtype=torch.bfloat16) -> int:
+    return int(lib().vggt_descriptor_xattn_workspace(S, T, Dn, H, kv_splits, BF16 if dtype == torch.bfloat16 else F32))
+
+
+def vggt_descriptor_xattn(q, kd, vd, out=None, scale=0.0, kv_splits=0, workspace=None, stream=None):
+    """All S*T queries attend to all S*Dn descriptors; returns out."""
+    S, T, H = _tok(q, "q")
+    S2, Dn, H2 = _tok(kd, "kd")
+    if (S2, H2) != (S, H) or _tok(vd, "vd") != (S, Dn, H) or kd.dtype != q.dtype or vd.dtype != q.dtype:
+        raise ValueError("kd/vd must be [S, Dn, H, 64] of q's dtype")
+    out = torch.empty_like(q) if out is None else out
+    if _tok(out, "out") != (S, T, H) or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    need = vggt_descriptor_xattn_workspace(S, T, Dn, H, kv_splits, q.dtype)
+    ws, nbytes = _workspace(need, q.device, workspace)
+    _check("vggt_descriptor_xattn",
+           lib().vggt_descriptor_xattn(_ptr(q), _ptr(kd), _ptr(vd), _ptr(out), _dtype_code(q), S, T, Dn, H, scale,
+                                       kv_splits, _ptr(ws), nbytes, _stream(stream)))
+    return out

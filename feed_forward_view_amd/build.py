@@ -1,0 +1,70 @@
+"""Build libvggt_attn.so (gfx950) in-tree with hipcc.
+
+    python -m feed_forward_view_amd.build
+
+Every HIP source is compiled for gfx950 only, with packed-fp32 instruction
+generation disabled, then linked into one shared library next to this file.
+"""
+from __future__ import annotations
+
+import concurrent.futures
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD_DIR = os.path.join(HERE, "_build")
+LIB = os.path.join(HERE, "libvggt_attn.so")
+
+SOURCES = ["capi.cpp", "attn_bf16.hip", "attn_f32.hip", "merge.hip", "rope.hip", "pool.hip"]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found")
+
+
+COMMON_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-fvisibility=hidden",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+    "-I", INCLUDE, "-I", CSRC,
+]
+
+
+def _compile(src: str) -> str:
+    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc(), "-x", "hip", *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    out = "\n".join(line for line in (r.stdout + r.stderr).splitlines()
+                    if "packed-fp32-ops" not in line and "not a recognized feature" not in line)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{out}")
+    if out.strip():
+        print(out, file=sys.stderr)
+    return obj
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    with concurrent.futures.ThreadPoolExecutor(min(8, len(SOURCES))) as ex:
+        objs = list(ex.map(_compile, SOURCES))
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB}")
+    return LIB
+
+
+if __name__ == "__main__":
+    build()

@@ -1,0 +1,72 @@
+// Internal declarations shared by the HIP sources of libvggt_attn (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vggt {
+
+constexpr int kHeadDim = 64;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// bf16 <-> fp32.  Widening is exact; narrowing rounds to nearest even
+// (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// One attention problem as the kernels see it.  Q/K/V/O are [tokens][H][64];
+// queries of sequence `s` are tokens [s*q_seq_stride, s*q_seq_stride + nq),
+// its keys are tokens [s*k_seq_stride, s*k_seq_stride + nk).  With
+// splits > 1 each workgroup covers keys_per_split keys of its sequence and
+// writes un-normalised fp32 partial outputs plus (max, sum) per row; a merge
+// kernel then combines them.
+struct AttnProblem {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;                 // final output (dtype of the call)
+  float* part_o;           // [splits][nq_total][H][64]
+  float* part_ml;          // [splits][nq_total][H][2]: (max in log2 units, sum)
+  int64_t tok_stride;      // elements between consecutive tokens (= H*64)
+  int64_t q_seq_stride;    // tokens between sequence starts of q / o
+  int64_t k_seq_stride;    // tokens between sequence starts of k / v
+  int64_t nq_total;        // query tokens over all sequences (partial rows)
+  int nq;                  // queries per sequence
+  int nk;                  // keys per sequence
+  int nseq;                // sequences
+  int H;                   // heads
+  int splits;              // key ranges per sequence
+  int keys_per_split;      // multiple of the key tile
+  float scale_log2;        // softmax scale * log2(e)
+};
+
+// Launchers (stream-ordered, no synchronisation).  Return hipSuccess or the
+// launch error.
+hipError_t launch_attn_bf16(const AttnProblem& p, hipStream_t stream);
+hipError_t launch_attn_f32(const AttnProblem& p, hipStream_t stream);
+hipError_t launch_attn_merge(const AttnProblem& p, bool out_bf16, hipStream_t stream);
+hipError_t launch_rope(const void* src, void* dst, bool bf16, int64_t n_tok, int T, int H, const int32_t* pos_yx,
+                       double base, hipStream_t stream);
+hipError_t launch_pool(const void* k, const void* v, void* kd, void* vd, bool bf16, int S, int T, int H, int gh,
+                       int gw, int patch_begin, int ph, int pw, int Dn, hipStream_t stream);
+
+// Query tile of the bf16 kernel and key tile of both kernels (the split size
+// must be a multiple of the key tile).
+constexpr int kAttnKeyTile = 64;
+int attn_bf16_query_tile();
+int attn_f32_query_tile();
+
+}  // namespace vggt

@@ -1,0 +1,155 @@
+/*
+ * vggt_attn.h -- C ABI of the MI355X (gfx950) alternating-attention library
+ * for VGGT-style feed-forward reconstruction models.
+ *
+ * The aggregator of these models alternates two softmax attentions over the
+ * tokens of S frames (the "VGGT 論文報告" slide deck, Section XI "架構",
+ * slide 3/7, "Global + Frame Attention"; the VGGT-JAX README's attention
+ * kernel-trial table shows them as [S, T, 16, 64] frame and [1, S*T, 16, 64]
+ * global attention):
+ *   - frame attention: each frame's T tokens attend to that frame only;
+ *   - global attention: all S*T tokens attend to all S*T tokens.
+ * The FlashVGGT variant (FlashVGGT README, "Overview") replaces global
+ * attention by cross-attention from every token to a compact per-frame set of
+ * spatially pooled descriptor keys/values.
+ *
+ * Tensor layout (every call): contiguous row-major [S, T, H, 64], i.e. token
+ * t of frame s, head h, channel c lives at ((s*T + t)*H + h)*64 + c.  The
+ * frame view and the global view are the same memory.  Head dim is 64
+ * (embed 1024 = 16 heads x 64, VGGT-Omega config article, field table).
+ *
+ * Element types: VGGT_BF16 (bf16 in/out, fp32 accumulation and softmax) or
+ * VGGT_F32 (fp32 in/out, fp32 arithmetic throughout; a debug mode for tight
+ * numerical comparison).
+ *
+ * Conventions for every call:
+ *   - Ownership: the caller owns all device buffers, including the workspace
+ *     sized by the matching *_workspace() query.  The library never allocates,
+ *     frees or synchronises.
+ *   - Streams: `stream` is a hipStream_t passed as void*; NULL means the null
+ *     stream.  Work is enqueued asynchronously on it.
+ *   - Errors: arguments are validated on the host before anything is
+ *     enqueued; a failed check returns a status, enqueues nothing and leaves
+ *     outputs untouched.  A failed launch returns VGGT_ERR_DEVICE; the detail
+ *     is in vggt_last_error() (thread-local).  No C++ exception crosses the ABI.
+ *   - Pointers: device pointers, 16-byte aligned.  Outputs must not overlap
+ *     inputs (VGGT_ERR_ALIAS), except that vggt_attn_rope works in place.
+ *   - Device: the current HIP device must be gfx950 (VGGT_ERR_UNSUPPORTED).
+ *   - Reentrancy: calls are reentrant; calls that share a workspace must be
+ *     ordered on one stream by the caller.
+ */
+#ifndef VGGT_ATTN_H
+#define VGGT_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VGGT_ATTN_ABI_VERSION 1
+#define VGGT_HEAD_DIM 64
+
+typedef enum {
+  VGGT_OK = 0,
+  VGGT_ERR_NULL = 1,        /* a required pointer is NULL */
+  VGGT_ERR_SHAPE = 2,       /* a size is out of range or inconsistent */
+  VGGT_ERR_UNSUPPORTED = 3, /* unsupported dtype or device (not gfx950) */
+  VGGT_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+  VGGT_ERR_ALIAS = 5,       /* an output overlaps an input */
+  VGGT_ERR_WORKSPACE = 6,   /* workspace missing or smaller than required */
+  VGGT_ERR_DEVICE = 7       /* a HIP call failed; see vggt_last_error() */
+} vggt_status;
+
+typedef enum { VGGT_BF16 = 0, VGGT_F32 = 1 } vggt_dtype;
+
+/* Returns VGGT_ATTN_ABI_VERSION of the built library. */
+int vggt_abi_version(void);
+/* Static string naming a status code. */
+const char* vggt_status_str(int status);
+/* Thread-local detail of the last failure on this thread ("" if none). */
+const char* vggt_last_error(void);
+
+/*
+ * 2D rotary position embedding, in place.
+ * Source: VGGT-Omega-1B-512-bf16 config article, input-parameter section
+ * (rope_base 100; the RoPE frequency buffers are fp32); frequency schedule of
+ * the "VGGT 論文報告" slide deck, Section IV, slide 4/6 (pair i of a width-d
+ * axis turns at pos / base^(2i/d)).
+ *   x       [S, T, H, 64] device, dtype dt; rotated in place.
+ *   pos_yx  [T, 2] int32 device: (row, col) of token t in every frame.
+ *   base    rope base (> 0).
+ * Channels 0..31 rotate by the row, 32..63 by the column; pair (2k, 2k+1) of
+ * a half turns by p * base^(-2k/32), k = 0..15.  Position (0, 0) is the
+ * identity, bit for bit.  Angles are formed in fp64, cos/sin rounded to fp32,
+ * the rotation done in fp32 and stored with round-to-nearest-even.
+ */
+vggt_status vggt_attn_rope(void* x, vggt_dtype dt, int S, int T, int H, const int32_t* pos_yx, float base,
+                           void* stream);
+
+/*
+ * Frame-wise attention: S independent sequences of T tokens (slide deck
+ * Section XI, slide 3/7; Section V, slide 5/10 for softmax(Q K^T / sqrt(d)) V,
+ * slide 9/10 for independent heads).  No mask.
+ *   q, k, v [S, T, H, 64] device, dtype dt (read only).
+ *   o       [S, T, H, 64] device, dtype dt (written).
+ *   pos_yx  [T, 2] int32 device or NULL (NULL: no RoPE); with positions, q
+ *           and k are rotated as in vggt_attn_rope before the product.
+ *   scale   softmax scale; <= 0 selects 1/sqrt(64) = 0.125.
+ *   workspace: device scratch of at least vggt_frame_attn_workspace(...) bytes
+ *           (may be NULL when that is 0).
+ */
+size_t vggt_frame_attn_workspace(int S, int T, int H, int rope_on, vggt_dtype dt);
+vggt_status vggt_frame_attn(const void* q, const void* k, const void* v, void* o, vggt_dtype dt, int S, int T,
+                            int H, const int32_t* pos_yx, float rope_base, float scale, void* workspace,
+                            size_t ws_bytes, void* stream);
+
+/*
+ * Global attention over all N = S*T tokens (slide deck Section XI, slide 3/7;
+ * Section V, slides 5/10 and 9/10).  Each token keeps its within-frame
+ * position for RoPE (frames carry no index of their own).
+ *   Arguments as for vggt_frame_attn, plus
+ *   kv_splits  number of key ranges computed by separate workgroups and merged
+ *              exactly by log-sum-exp; 0 lets the library choose (1..64).
+ */
+size_t vggt_global_attn_workspace(int S, int T, int H, int kv_splits, int rope_on, vggt_dtype dt);
+vggt_status vggt_global_attn(const void* q, const void* k, const void* v, void* o, vggt_dtype dt, int S, int T,
+                             int H, const int32_t* pos_yx, float rope_base, float scale, int kv_splits,
+                             void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * FlashVGGT descriptor pooling (FlashVGGT README, "Overview": each frame's
+ * spatial information is compressed into a compact descriptor set; "Key
+ * Arguments": --kv_downfactor, default 4, taken here as a ph x pw = 2 x 2
+ * token-count factor).
+ *   k, v    [S, T, H, 64] device, dtype dt; the patch grid is tokens
+ *           [patch_begin, patch_begin + gh*gw) of each frame, row-major.
+ *   kd, vd  [S, Dn, H, 64] device, Dn = vggt_descriptor_count(T, gh, gw, ph, pw):
+ *           first the T - gh*gw special tokens copied in order, then one
+ *           descriptor per ph x pw window (row-major over ceil(gh/ph) x
+ *           ceil(gw/pw) windows) holding the mean of the window's cells that
+ *           lie inside the grid.  Sums in fp32, stored with round-to-nearest-even.
+ */
+int vggt_descriptor_count(int T, int gh, int gw, int ph, int pw);
+vggt_status vggt_descriptor_pool(const void* k, const void* v, void* kd, void* vd, vggt_dtype dt, int S, int T,
+                                 int H, int gh, int gw, int patch_begin, int ph, int pw, void* stream);
+
+/*
+ * FlashVGGT descriptor cross-attention (FlashVGGT README, "Overview": global
+ * attention becomes cross-attention between all image tokens and the smaller
+ * descriptor set).  All S*T query tokens attend to all S*Dn descriptors; no
+ * RoPE inside (rotate q and k with vggt_attn_rope before pooling if wanted).
+ *   q   [S, T, H, 64]; kd, vd [S, Dn, H, 64]; o [S, T, H, 64]; dtype dt.
+ *   scale, kv_splits, workspace as for vggt_global_attn.
+ */
+size_t vggt_descriptor_xattn_workspace(int S, int T, int Dn, int H, int kv_splits, vggt_dtype dt);
+vggt_status vggt_descriptor_xattn(const void* q, const void* kd, const void* vd, void* o, vggt_dtype dt, int S,
+                                  int T, int Dn, int H, float scale, int kv_splits, void* workspace,
+                                  size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VGGT_ATTN_H */

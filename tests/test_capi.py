@@ -1,0 +1,122 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function the header declares, and rejects bad arguments with the
+documented status before touching the device."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import feed_forward_view_amd as ffv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vggt_attn.h")
+
+OK, NULL, SHAPE, UNSUP, ALIGN, ALIAS, WS = 0, 1, 2, 3, 4, 5, 6
+
+
+def header_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(vggt_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(ffv.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return ffv.lib()
+
+
+def test_exports_match_header(L):
+    declared = header_functions()
+    assert len(declared) == 12
+    out = subprocess.run(["nm", "-D", "--defined-only", ffv.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = sorted(set(m for m in re.findall(r"\bT (vggt_\w+)", out)))
+    assert exported == declared
+    assert sorted(ffv.SIGNATURES) == declared
+
+
+def test_version_and_status_strings(L):
+    assert L.vggt_abi_version() == 1
+    for code, name in ffv.STATUS.items():
+        assert L.vggt_status_str(code).decode() == name
+    assert L.vggt_status_str(99).decode() == "VGGT_ERR_UNKNOWN"
+
+
+def test_descriptor_count(L):
+    assert L.vggt_descriptor_count(1374, 37, 37, 2, 2) == 366
+    assert L.vggt_descriptor_count(1040, 32, 32, 2, 2) == 16 + 256
+    assert L.vggt_descriptor_count(261, 16, 16, 1, 1) == 261
+    assert L.vggt_descriptor_count(10, 4, 4, 2, 2) == -1  # grid larger than T
+
+
+def test_workspace_queries(L):
+    # frame: two rotated copies with RoPE, nothing without
+    assert L.vggt_frame_attn_workspace(4, 261, 16, 0, 0) == 0
+    assert L.vggt_frame_attn_workspace(4, 261, 16, 1, 0) >= 2 * 4 * 261 * 16 * 64 * 2
+    # global with one split and no RoPE needs nothing
+    assert L.vggt_global_attn_workspace(32, 1374, 16, 1, 0, 0) == 0
+    # explicit splits need the fp32 partials
+    n = 4 * 261
+    assert L.vggt_global_attn_workspace(4, 261, 16, 3, 0, 0) >= 3 * n * 16 * (64 + 2) * 4
+    assert L.vggt_descriptor_xattn_workspace(100, 1374, 366, 16, 1, 0) == 0
+    # invalid arguments give 0
+    assert L.vggt_global_attn_workspace(4, 261, 16, 65, 0, 0) == 0
+    assert L.vggt_frame_attn_workspace(4, 0, 16, 1, 0) == 0
+
+
+def _p(addr):
+    return ctypes.c_void_p(addr)
+
+
+A = 0x100000  # fake, aligned, never dereferenced: every call below fails validation first
+B = 0x200000
+C = 0x300000
+O = 0x400000
+
+
+def test_rejects_bad_arguments_without_device(L):
+    f = L.vggt_frame_attn
+    # null pointer
+    assert f(None, _p(B), _p(C), _p(O), 0, 2, 8, 1, None, 100.0, 0.0, None, 0, None) == NULL
+    # bad shapes / dtype
+    assert f(_p(A), _p(B), _p(C), _p(O), 0, 2, 0, 1, None, 100.0, 0.0, None, 0, None) == SHAPE
+    assert f(_p(A), _p(B), _p(C), _p(O), 0, -1, 8, 1, None, 100.0, 0.0, None, 0, None) == SHAPE
+    assert f(_p(A), _p(B), _p(C), _p(O), 0, 2, 8, 0, None, 100.0, 0.0, None, 0, None) == SHAPE
+    assert f(_p(A), _p(B), _p(C), _p(O), 7, 2, 8, 1, None, 100.0, 0.0, None, 0, None) == UNSUP
+    # misaligned
+    assert f(_p(A + 2), _p(B), _p(C), _p(O), 0, 2, 8, 1, None, 100.0, 0.0, None, 0, None) == ALIGN
+    # output aliases an input
+    assert f(_p(A), _p(B), _p(C), _p(A + 64), 0, 2, 8, 1, None, 100.0, 0.0, None, 0, None) == ALIAS
+    # RoPE needs a workspace; too small one
+    pos = _p(0x500000)
+    assert f(_p(A), _p(B), _p(C), _p(O), 0, 2, 8, 1, pos, 100.0, 0.0, None, 0, None) == WS
+    assert f(_p(A), _p(B), _p(C), _p(O), 0, 2, 8, 1, pos, 100.0, 0.0, _p(0x600000), 16, None) == WS
+    # bad rope base
+    assert f(_p(A), _p(B), _p(C), _p(O), 0, 2, 8, 1, pos, -1.0, 0.0, _p(0x600000), 1 << 20, None) == SHAPE
+    # S == 0 is a no-op
+    assert f(None, None, None, None, 0, 0, 8, 1, None, 100.0, 0.0, None, 0, None) == OK
+
+    g = L.vggt_global_attn
+    assert g(_p(A), _p(B), _p(C), _p(O), 0, 2, 8, 1, None, 100.0, 0.0, 65, None, 0, None) == SHAPE
+    assert g(_p(A), _p(B), _p(C), _p(O), 0, 2, 8, 1, None, 100.0, 0.0, -1, None, 0, None) == SHAPE
+    assert g(_p(A), _p(B), _p(C), _p(O), 0, 64, 64, 1, None, 100.0, 0.0, 4, None, 0, None) == WS
+
+    r = L.vggt_attn_rope
+    assert r(_p(A), 0, 2, 8, 1, None, 100.0, None) == NULL
+    assert r(_p(A), 0, 2, 8, 1, _p(0x500000), 0.0, None) == SHAPE
+    assert r(_p(A + 8), 0, 2, 8, 1, _p(0x500000), 100.0, None) == ALIGN
+
+    pl = L.vggt_descriptor_pool
+    assert pl(_p(A), _p(B), None, _p(O), 0, 2, 14, 1, 3, 4, 2, 2, 2, None) == NULL
+    assert pl(_p(A), _p(B), _p(C), _p(O), 0, 2, 14, 1, 3, 4, 3, 2, 2, None) == SHAPE  # grid past T
+    assert pl(_p(A), _p(B), _p(A), _p(O), 0, 2, 14, 1, 3, 4, 2, 2, 2, None) == ALIAS
+
+    x = L.vggt_descriptor_xattn
+    assert x(_p(A), _p(B), _p(C), _p(O), 0, 2, 8, 0, 1, 0.0, 0, None, 0, None) == SHAPE
+    assert x(_p(A), _p(B), _p(C), _p(B), 0, 2, 8, 3, 1, 0.0, 1, None, 0, None) == ALIAS
+    assert L.vggt_last_error().decode() != ""

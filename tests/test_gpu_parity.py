@@ -1,0 +1,330 @@
+"""GPU parity: the HIP library (through the C ABI) against the float64 oracle.
+
+bf16 bar: max |gpu - oracle| <= 2e-2 and mean |gpu - oracle| <= 2e-3 per
+output tensor, for unit-normal Q/K/V.  fp32 debug bar: NRMSE <= 1e-5
+(sqrt(mean(err^2)) / sqrt(mean(ref^2))).  Small shapes are compared in full;
+the full-size workloads are compared on sampled query rows (every special
+token of the first and last frame, the first and last rows, the rows around
+query-tile boundaries, the last partial tile and seeded random rows) in the
+launch configuration the benchmark times.
+"""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import feed_forward_view_amd as ffv
+import oracle
+import workload
+
+pytestmark = pytest.mark.gpu
+
+BF16_MAX, BF16_MEAN, F32_NRMSE = 2e-2, 2e-3, 1e-5
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ffv.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def to_dev(a: np.ndarray) -> torch.Tensor:
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev()).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev())
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    torch.cuda.synchronize()
+    if t.dtype == torch.bfloat16:
+        return oracle.to_f64(t.view(torch.int16).cpu().numpy().view(np.uint16))
+    return t.cpu().numpy().astype(np.float64)
+
+
+def check_bf16(got: np.ndarray, ref: np.ndarray, label: str):
+    err = np.abs(got.reshape(ref.shape) - ref)
+    mx, mean = float(err.max()), float(err.mean())
+    print(f"{label}: max_abs {mx:.3e} mean_abs {mean:.3e} (ref max {np.abs(ref).max():.3f})")
+    assert np.isfinite(got).all(), label
+    assert mx <= BF16_MAX and mean <= BF16_MEAN, f"{label}: max {mx:.3e} mean {mean:.3e}"
+
+
+def check_f32(got: np.ndarray, ref: np.ndarray, label: str):
+    diff = got.reshape(ref.shape) - ref
+    nrmse = float(np.sqrt(np.mean(diff ** 2)) / max(np.sqrt(np.mean(ref ** 2)), 1e-30))
+    print(f"{label}: nrmse {nrmse:.3e} max_abs {np.abs(diff).max():.3e}")
+    assert nrmse <= F32_NRMSE, f"{label}: nrmse {nrmse:.3e}"
+
+
+def sample_rows(n: int, T: int, S: int, seed: int, n_random: int = 96, tile: int = 256) -> np.ndarray:
+    rows = set(range(min(5, n)))
+    rows |= {(S - 1) * T + t for t in range(min(5, T))}
+    rows |= {0, n - 1}
+    for b in range(tile, n, tile * max(1, (n // tile) // 8)):
+        rows |= {b - 1, b, b + 1}
+    last = (n - 1) // tile * tile
+    rows |= set(range(last, n, max(1, (n - last) // 8)))
+    rng = np.random.default_rng(seed)
+    rows |= set(int(x) for x in rng.integers(0, n, size=n_random))
+    return np.array(sorted(r for r in rows if 0 <= r < n), dtype=np.int64)
+
+
+@functools.lru_cache(maxsize=2)
+def inputs(name: str):
+    wl = workload.WORKLOADS[name]
+    q, k, v = wl.qkv_bf16()
+    return wl, q, k, v
+
+
+# ---------------------------------------------------------------------------
+# RoPE
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_rope_against_oracle(dtype):
+    wl = workload.WORKLOADS["vggt-518-s8"]
+    S = 2
+    x = workload.normal_bf16(wl.seed("q"), (S, wl.T, 16, 64))
+    if dtype == "f32":
+        x = workload.bf16_bits_to_f32(x).reshape(x.shape)
+    pos = wl.positions()
+    xd = to_dev(x)
+    ffv.vggt_attn_rope(xd, torch.from_numpy(pos).to(dev()), 100.0)
+    got = to_f64(xd).reshape(S * wl.T, 16, 64)
+    ref = oracle.rope(oracle.to_f64(x).reshape(S * wl.T, 16, 64), np.tile(pos, (S, 1)), 100.0)
+    xin = oracle.to_f64(x).reshape(S * wl.T, 16, 64)
+    # fp32 rotation error, relative to the magnitude of the rotated pair
+    pair = np.abs(xin) + np.abs(xin.reshape(-1, 2)[:, ::-1].reshape(xin.shape))
+    eps32 = 2.0 ** -21 * pair
+    if dtype == "bf16":
+        # one fp32 rotation then one rounding to bf16: within half a bf16 ulp
+        # (plus the fp32 error) of the exact value, and equal to its
+        # round-to-nearest-even almost everywhere
+        mag = np.maximum(np.maximum(np.abs(ref), np.abs(got)), 1e-30)
+        ulp = np.exp2(np.floor(np.log2(mag)) - 7)
+        excess = np.abs(got - ref) - (0.5 * ulp + eps32)
+        assert excess.max() <= 0, f"rope bf16: worst excess {excess.max():.3e}"
+        rne = oracle.to_f64(workload.f32_to_bf16_bits(ref.astype(np.float32))).reshape(ref.shape)
+        frac = float(np.mean(got == rne))
+        print(f"rope bf16: exact-RNE fraction {frac:.6f}")
+        assert frac >= 0.999
+    else:
+        excess = np.abs(got - ref) - (2.0 ** -23 * np.abs(ref) + eps32)
+        assert excess.max() <= 0, f"rope f32: worst excess {excess.max():.3e}"
+    # special tokens (position (0,0)) are untouched, bit for bit
+    specials = np.concatenate([np.arange(5) + s * wl.T for s in range(S)])
+    np.testing.assert_array_equal(got[specials], xin[specials])
+
+
+# ---------------------------------------------------------------------------
+# Frame / global attention, small shapes compared in full
+# ---------------------------------------------------------------------------
+
+def test_frame_and_global_small_full():
+    wl, q, k, v = inputs("vggt-224-s4")
+    pos = wl.positions()
+    qd, kd, vd, pd = to_dev(q), to_dev(k), to_dev(v), torch.from_numpy(pos).to(dev())
+    fo = to_f64(ffv.vggt_frame_attn(qd, kd, vd, pos_yx=pd, rope_base=100.0))
+    check_bf16(fo, oracle.frame_attn(q, k, v, wl.S, wl.T, pos=pos), "frame 4x261")
+    ref_g = oracle.global_attn(q, k, v, wl.S, wl.T, pos=pos)
+    for splits in (0, 1, 2, 3, 7):
+        go = to_f64(ffv.vggt_global_attn(qd, kd, vd, pos_yx=pd, rope_base=100.0, kv_splits=splits))
+        check_bf16(go, ref_g, f"global N=1044 splits={splits}")
+
+
+@pytest.mark.parametrize("T", [1, 5, 63, 64, 65, 129, 257])
+@pytest.mark.parametrize("H", [1, 3])
+def test_ragged_shapes(T, H):
+    S = 3
+    seed = 1000 + 10 * T + H
+    q = workload.normal_bf16(seed, (S, T, H, 64))
+    k = workload.normal_bf16(seed + 1, (S, T, H, 64))
+    v = workload.normal_bf16(seed + 2, (S, T, H, 64))
+    gh = max(1, int(np.sqrt(max(T - 2, 1))))
+    gw = max(1, (T - 2) // gh) if T > 2 else 1
+    pb = T - gh * gw
+    pos = workload.positions(T, gh, gw, pb)
+    qd, kd, vd, pd = to_dev(q), to_dev(k), to_dev(v), torch.from_numpy(pos).to(dev())
+    for use_pos in (True, False):
+        p_host = pos if use_pos else None
+        p_dev = pd if use_pos else None
+        fo = to_f64(ffv.vggt_frame_attn(qd, kd, vd, pos_yx=p_dev))
+        check_bf16(fo, oracle.frame_attn(q, k, v, S, T, pos=p_host), f"frame T={T} H={H} rope={use_pos}")
+        ref = oracle.global_attn(q, k, v, S, T, pos=p_host)
+        for splits in (1, 2):
+            go = to_f64(ffv.vggt_global_attn(qd, kd, vd, pos_yx=p_dev, kv_splits=splits))
+            check_bf16(go, ref, f"global T={T} H={H} rope={use_pos} splits={splits}")
+
+
+def test_single_token_frames_return_values():
+    q = workload.normal_bf16(5, (4, 1, 2, 64))
+    v = workload.normal_bf16(6, (4, 1, 2, 64))
+    out = ffv.vggt_frame_attn(to_dev(q), to_dev(q), to_dev(v))
+    np.testing.assert_array_equal(to_f64(out), oracle.to_f64(v))
+
+
+def test_scale_argument():
+    wl = workload.Workload("t", 21, S=2, gh=6, gw=6, n_special=5, patch_begin=5, H=2)
+    q, k, v = wl.qkv_bf16()
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    ref = oracle.global_attn(q, k, v, wl.S, wl.T, scale=0.3)
+    check_bf16(to_f64(ffv.vggt_global_attn(qd, kd, vd, scale=0.3)), ref, "global scale=0.3")
+
+
+def test_deterministic_repeat():
+    wl, q, k, v = inputs("vggt-224-s4")
+    pos = torch.from_numpy(wl.positions()).to(dev())
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    a = ffv.vggt_global_attn(qd, kd, vd, pos_yx=pos, kv_splits=3)
+    b = ffv.vggt_global_attn(qd, kd, vd, pos_yx=pos, kv_splits=3)
+    c = ffv.vggt_frame_attn(qd, kd, vd, pos_yx=pos)
+    d = ffv.vggt_frame_attn(qd, kd, vd, pos_yx=pos)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert torch.equal(c.view(torch.int16), d.view(torch.int16))
+
+
+def test_frame_permutation_equivariance_gpu():
+    wl, q, k, v = inputs("vggt-224-s4")
+    pos = torch.from_numpy(wl.positions()).to(dev())
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    perm = torch.tensor([2, 0, 3, 1], device=dev())
+    g = ffv.vggt_global_attn(qd, kd, vd, pos_yx=pos, kv_splits=1)
+    gp = ffv.vggt_global_attn(qd[perm].contiguous(), kd[perm].contiguous(), vd[perm].contiguous(), pos_yx=pos,
+                              kv_splits=1)
+    err = (gp.float() - g[perm].float()).abs().max().item()
+    assert err <= 2 * 2.0 ** -8, err  # equal up to the summation order of the keys
+
+
+# ---------------------------------------------------------------------------
+# fp32 debug mode
+# ---------------------------------------------------------------------------
+
+def test_f32_debug_mode():
+    wl = workload.Workload("t", 22, S=3, gh=9, gw=11, n_special=5, patch_begin=5, H=2)
+    q, k, v = wl.qkv_f32()
+    pos = wl.positions()
+    qd, kd, vd, pd = to_dev(q), to_dev(k), to_dev(v), torch.from_numpy(pos).to(dev())
+    check_f32(to_f64(ffv.vggt_frame_attn(qd, kd, vd, pos_yx=pd)), oracle.frame_attn(q, k, v, wl.S, wl.T, pos=pos),
+              "f32 frame")
+    ref = oracle.global_attn(q, k, v, wl.S, wl.T, pos=pos)
+    for splits in (1, 3):
+        check_f32(to_f64(ffv.vggt_global_attn(qd, kd, vd, pos_yx=pd, kv_splits=splits)), ref,
+                  f"f32 global splits={splits}")
+    kp, vp = ffv.vggt_descriptor_pool(kd, vd, 9, 11, 5, 2, 2)
+    kpr = oracle.descriptor_pool(k, wl.S, wl.T, 9, 11, 5, 2, 2)
+    vpr = oracle.descriptor_pool(v, wl.S, wl.T, 9, 11, 5, 2, 2)
+    check_f32(to_f64(kp), kpr, "f32 pool k")
+    check_f32(to_f64(ffv.vggt_descriptor_xattn(qd, kp, vp, kv_splits=2)), oracle.descriptor_xattn(q, kpr, vpr),
+              "f32 xattn")
+
+
+# ---------------------------------------------------------------------------
+# Descriptor pooling and cross-attention
+# ---------------------------------------------------------------------------
+
+def _pool_check(got_bits_f64, ref, label):
+    # fp32 sum then one rounding: within one bf16 ulp of the exact mean, and
+    # equal to its round-to-nearest-even almost everywhere
+    ref32 = ref.astype(np.float32)
+    rne = oracle.to_f64(workload.f32_to_bf16_bits(ref32)).reshape(ref.shape)
+    got = got_bits_f64.reshape(ref.shape)
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 7)
+    bad = int(np.sum(np.abs(got - ref) > ulp))
+    assert bad == 0, f"{label}: {bad} elements beyond one bf16 ulp"
+    frac = float(np.mean(got == rne))
+    print(f"{label}: exact-RNE fraction {frac:.6f}")
+    assert frac >= 0.9999, label
+
+
+def test_pool_small_grids():
+    for (gh, gw, pb, ns, ph, pw) in [(37, 37, 5, 5, 2, 2), (5, 7, 3, 3, 2, 2), (4, 4, 0, 16, 2, 2), (6, 5, 1, 2, 3, 2),
+                                     (3, 3, 0, 0, 1, 1)]:
+        S, H = 2, 16
+        T = gh * gw + ns
+        k = workload.normal_bf16(77 + gh, (S, T, H, 64))
+        v = workload.normal_bf16(78 + gh, (S, T, H, 64))
+        kp, vp = ffv.vggt_descriptor_pool(to_dev(k), to_dev(v), gh, gw, pb, ph, pw)
+        _pool_check(to_f64(kp), oracle.descriptor_pool(k, S, T, gh, gw, pb, ph, pw), f"pool k {gh}x{gw}/{ph}x{pw}")
+        _pool_check(to_f64(vp), oracle.descriptor_pool(v, S, T, gh, gw, pb, ph, pw), f"pool v {gh}x{gw}/{ph}x{pw}")
+
+
+def test_xattn_small_full_and_unit_window():
+    wl = workload.Workload("t", 23, S=3, gh=12, gw=12, n_special=5, patch_begin=5, H=4)
+    q, k, v = wl.qkv_bf16()
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    kp, vp = ffv.vggt_descriptor_pool(kd, vd, 12, 12, 5, 2, 2)
+    kpr = oracle.descriptor_pool(k, wl.S, wl.T, 12, 12, 5, 2, 2)
+    vpr = oracle.descriptor_pool(v, wl.S, wl.T, 12, 12, 5, 2, 2)
+    # the oracle sees the GPU's own bf16 descriptors, so only the attention is compared
+    ref = oracle.descriptor_xattn(q, to_f64(kp), to_f64(vp))
+    for splits in (0, 1, 3):
+        check_bf16(to_f64(ffv.vggt_descriptor_xattn(qd, kp, vp, kv_splits=splits)), ref, f"xattn splits={splits}")
+    # and end to end against the oracle's own pooled descriptors
+    check_bf16(to_f64(ffv.vggt_descriptor_xattn(qd, kp, vp)), oracle.descriptor_xattn(q, kpr, vpr), "xattn e2e")
+    # unit window: descriptor attention equals global attention without RoPE
+    k1, v1 = ffv.vggt_descriptor_pool(kd, vd, 12, 12, 5, 1, 1)
+    a = to_f64(ffv.vggt_descriptor_xattn(qd, k1, v1, kv_splits=1))
+    check_bf16(a, oracle.global_attn(q, k, v, wl.S, wl.T), "xattn unit window vs global")
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads on sampled rows
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["vggt-518-s8", "vggt-518-s32", "omega-512-s64"])
+def test_full_size_frame_and_global(name):
+    wl, q, k, v = inputs(name)
+    pos = wl.positions()
+    qd, kd, vd, pd = to_dev(q), to_dev(k), to_dev(v), torch.from_numpy(pos).to(dev())
+    rows = sample_rows(wl.N, wl.T, wl.S, seed=wl.index, n_random=64)
+    fo = ffv.vggt_frame_attn(qd, kd, vd, pos_yx=pd, rope_base=100.0)
+    got = to_f64(fo).reshape(wl.N, wl.H, 64)[rows]
+    check_bf16(got, oracle.frame_attn(q, k, v, wl.S, wl.T, pos=pos, rows=rows), f"{name} frame ({rows.size} rows)")
+    del fo
+    go = ffv.vggt_global_attn(qd, kd, vd, pos_yx=pd, rope_base=100.0)
+    got = to_f64(go).reshape(wl.N, wl.H, 64)[rows]
+    check_bf16(got, oracle.global_attn(q, k, v, wl.S, wl.T, pos=pos, rows=rows), f"{name} global ({rows.size} rows)")
+
+
+def test_full_size_descriptor_path():
+    wl, q, k, v = inputs("flashvggt-518-s100")
+    ph, pw = wl.pool
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    kp, vp = ffv.vggt_descriptor_pool(kd, vd, wl.gh, wl.gw, wl.patch_begin, ph, pw)
+    Dn = kp.shape[1]
+    assert Dn == 366
+    kpr = oracle.descriptor_pool(k, wl.S, wl.T, wl.gh, wl.gw, wl.patch_begin, ph, pw)
+    _pool_check(to_f64(kp), kpr, "s100 pool k")
+    vpr = oracle.descriptor_pool(v, wl.S, wl.T, wl.gh, wl.gw, wl.patch_begin, ph, pw)
+    _pool_check(to_f64(vp), vpr, "s100 pool v")
+    xo = ffv.vggt_descriptor_xattn(qd, kp, vp)
+    rows = sample_rows(wl.N, wl.T, wl.S, seed=wl.index, n_random=48)
+    got = to_f64(xo).reshape(wl.N, wl.H, 64)[rows]
+    qs = q.reshape(wl.N, wl.H, 64)[rows]
+    ref = oracle.attention(qs, kpr.reshape(-1, wl.H, 64), vpr.reshape(-1, wl.H, 64))
+    check_bf16(got, ref, f"s100 xattn ({rows.size} rows)")
+
+
+def test_split_count_independence_full_size():
+    wl, q, k, v = inputs("vggt-518-s8")
+    pos = wl.positions()
+    qd, kd, vd, pd = to_dev(q), to_dev(k), to_dev(v), torch.from_numpy(pos).to(dev())
+    rows = sample_rows(wl.N, wl.T, wl.S, seed=3, n_random=32)
+    ref = oracle.global_attn(q, k, v, wl.S, wl.T, pos=pos, rows=rows)
+    outs = []
+    for splits in (1, 2, 3, 7):
+        go = ffv.vggt_global_attn(qd, kd, vd, pos_yx=pd, kv_splits=splits)
+        outs.append(go.float())
+        check_bf16(to_f64(go).reshape(wl.N, wl.H, 64)[rows], ref, f"s8 global splits={splits}")
+    for o in outs[1:]:
+        # different split counts only reorder fp32 sums: results agree to bf16 rounding
+        assert (o - outs[0]).abs().max().item() <= 2.0 ** -7
