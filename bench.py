@@ -1,0 +1,220 @@
+"""Benchmark of the alternating-attention hot path on one MI355X.
+
+One step = one pass over every call of the path on one batch of 32 frames of
+518x518 (VGGT-1B shape: 37x37 patches + 1 camera + 4 register tokens = 1374
+tokens per frame, N = 43968, 16 heads of 64, bf16, 2D RoPE base 100):
+
+  frame attention (RoPE)      32 x 1374^2           247.4 GFLOP
+  global attention (RoPE)     43968^2              7917.8 GFLOP
+  descriptor pooling of K, V  2x2 windows -> 32 x 366 descriptors
+  descriptor cross-attention  43968 x 11712        2109.2 GFLOP
+
+FLOP = 4 * Nq * Nk * H * 64 (QK^T plus PV, 2 flop per multiply-add).  Inputs
+are seeded N(0,1) bf16 tensors already resident in HBM.  `value` is the
+step's algorithmic attention TFLOP/s over the timed region; per-call times
+come from HIP events recorded on the launch stream.  The oracle (float64, CPU)
+is timed on a row sample of the same step as the CPU baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "global-attention TFLOP/s + ms/layer at S frames; % of bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def attn_flops(nq: int, nk: int, H: int = 16, d: int = 64) -> float:
+    return 4.0 * nq * nk * H * d
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="vggt-518-s32")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-row-stride", type=int, default=48)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the path has no multi-GPU execution in this library "
+              "(see the sharding notes); run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import feed_forward_view_amd as ffv
+    import workload
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+    wl = workload.WORKLOADS[args.workload]
+    S, T, H, N = wl.S, wl.T, wl.H, wl.N
+    ph, pw = 2, 2
+
+    t0 = time.time()
+    q, k, v = wl.qkv_bf16()
+    gen_s = time.time() - t0
+    pos = wl.positions()
+
+    def to_dev(a):
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    posd = torch.from_numpy(pos).to(dev)
+    Dn = ffv.vggt_descriptor_count(T, wl.gh, wl.gw, ph, pw)
+    fo = torch.empty_like(qd)
+    go = torch.empty_like(qd)
+    xo = torch.empty_like(qd)
+    kpool = torch.empty((S, Dn, H, 64), dtype=torch.bfloat16, device=dev)
+    vpool = torch.empty_like(kpool)
+    ws_f = torch.empty(max(1, ffv.vggt_frame_attn_workspace(S, T, H, True)), dtype=torch.uint8, device=dev)
+    ws_g = torch.empty(max(1, ffv.vggt_global_attn_workspace(S, T, H, 0, True)), dtype=torch.uint8, device=dev)
+    ws_x = torch.empty(max(1, ffv.vggt_descriptor_xattn_workspace(S, T, Dn, H, 0)), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    calls = ["frame", "global", "pool", "xattn"]
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record(stream)
+        mark(0)
+        ffv.vggt_frame_attn(qd, kd, vd, out=fo, pos_yx=posd, rope_base=100.0, workspace=ws_f)
+        mark(1)
+        ffv.vggt_global_attn(qd, kd, vd, out=go, pos_yx=posd, rope_base=100.0, kv_splits=0, workspace=ws_g)
+        mark(2)
+        ffv.vggt_descriptor_pool(kd, vd, wl.gh, wl.gw, wl.patch_begin, ph, pw, kd=kpool, vd=vpool)
+        mark(3)
+        ffv.vggt_descriptor_xattn(qd, kpool, vpool, out=xo, kv_splits=0, workspace=ws_x)
+        mark(4)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+
+    per_call = {c: [] for c in calls}
+    for ev in events:
+        for j, c in enumerate(calls):
+            per_call[c].append(ev[j].elapsed_time(ev[j + 1]))
+    med = {c: float(np.median(x)) for c, x in per_call.items()}
+
+    flops = {
+        "frame": attn_flops(T, T) * S,
+        "global": attn_flops(N, N),
+        "xattn": attn_flops(N, S * Dn),
+    }
+    step_flops = sum(flops.values())
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+    g_tflops = flops["global"] / (med["global"] * 1e-3) / 1e12
+    pool_bytes = 2 * (S * T * H * 64 * 2) + 2 * (S * Dn * H * 64 * 2)  # read K, V; write Kd, Vd
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded SplitMix64/Box-Muller N(0,1) Q/K/V, bf16)",
+        "config": {
+            "workload": f"{wl.name}: S={S} frames x T={T} tokens (37x37 patches + 1 camera + 4 register), "
+                        f"N={N}, H={H}, d=64, RoPE base 100; step = frame + global attention + "
+                        f"2x2 descriptor pool + descriptor cross-attention ({S * Dn} descriptors)",
+            "S": S, "T": T, "N": N, "H": H, "head_dim": 64,
+        },
+        "ms_per_layer": round(med["frame"] + med["global"], 4),
+        "calls_ms_median": {c: round(x, 4) for c, x in med.items()},
+        "global_attention_tflops": round(g_tflops, 2),
+        "global_frac_of_bf16_peak": round(g_tflops / PEAK_BF16_TFLOPS, 4),
+        "frame_attention_tflops": round(flops["frame"] / (med["frame"] * 1e-3) / 1e12, 2),
+        "xattn_tflops": round(flops["xattn"] / (med["xattn"] * 1e-3) / 1e12, 2),
+        "pool_gbs": round(pool_bytes / (med["pool"] * 1e-3) / 1e9, 1),
+        "roofline": {
+            "kernel": "global attention call (attention kernel + RoPE pre-pass)",
+            "bound": "mfma",
+            "achieved": round(g_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(g_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+        },
+        "device": {"name": props.name, "cus": props.multi_processor_count,
+                   "arch": getattr(props, "gcnArchName", "")},
+        "input_gen_s": round(gen_s, 2),
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"], result["parity_sample"] = cpu_baseline(wl, q, k, v, pos, Dn, ph, pw, go, fo, xo,
+                                                                       args.cpu_row_stride)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def cpu_baseline(wl, q, k, v, pos, Dn, ph, pw, go, fo, xo, stride):
+    """The float64 oracle, untuned, on every `stride`-th query row of each
+    attention call of the step (plus the pooling of those rows' frames is not
+    needed: the oracle pools all frames), timed on the host cores."""
+    import torch
+
+    import oracle
+
+    S, T, H, N = wl.S, wl.T, wl.H, wl.N
+    nthreads = oracle.default_threads()
+    rows = np.arange(0, N, stride, dtype=np.int64)
+    t0 = time.perf_counter()
+    ref_f = oracle.frame_attn(q, k, v, S, T, pos=pos, base=100.0, rows=rows, nthreads=nthreads)
+    ref_g = oracle.global_attn(q, k, v, S, T, pos=pos, base=100.0, rows=rows, nthreads=nthreads)
+    kp = oracle.descriptor_pool(k, S, T, wl.gh, wl.gw, wl.patch_begin, ph, pw)
+    vp = oracle.descriptor_pool(v, S, T, wl.gh, wl.gw, wl.patch_begin, ph, pw)
+    ref_x = oracle.descriptor_xattn(q[:, :, :, :].reshape(N, H, 64)[rows], kp, vp, nthreads=nthreads)
+    secs = time.perf_counter() - t0
+    sampled_flops = rows.size * (attn_flops(1, T) + attn_flops(1, N) + attn_flops(1, S * Dn))
+    base = {
+        "value": round(sampled_flops / secs / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": nthreads,
+        "kind": "oracle",
+        "sample": f"every {stride}th query row ({rows.size} of {N}) of frame, global and descriptor attention, "
+                  f"all heads, plus full descriptor pooling; {secs:.1f} s",
+    }
+
+    def host(t):
+        return oracle.to_f64(t.view(torch.int16).cpu().numpy().view(np.uint16)).reshape(N, H, 64)[rows]
+
+    par = {}
+    for name, got, ref in (("frame", fo, ref_f), ("global", go, ref_g), ("xattn", xo, ref_x)):
+        err = np.abs(host(got) - ref.reshape(rows.size, H, 64))
+        par[name] = {"max_abs": float(err.max()), "mean_abs": float(err.mean())}
+    return base, par
+
+
+if __name__ == "__main__":
+    sys.exit(main())

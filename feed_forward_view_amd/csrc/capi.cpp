@@ -20,13 +20,6 @@ namespace {
 
 thread_local char g_last_error[512] = "";
 
-void set_error(const char* fmt, ...) {
-  va_list ap;
-  va_start(ap, fmt);
-  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
-  va_end(ap);
-}
-
 vggt_status fail(vggt_status s, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
@@ -128,11 +121,6 @@ SplitPlan plan_splits(int64_t nq, int64_t nk, int H, int requested, vggt_dtype d
   return p;
 }
 
-size_t partial_bytes(int64_t nq, int H, int splits) {
-  if (splits <= 1) return 0;
-  return align256((size_t)splits * nq * H * vggt::kHeadDim * 4) + align256((size_t)splits * nq * H * 2 * 4);
-}
-
 hipError_t run_attention(const vggt::AttnProblem& p, vggt_dtype dt, hipStream_t st) {
   hipError_t e = dt == VGGT_F32 ? vggt::launch_attn_f32(p, st) : vggt::launch_attn_bf16(p, st);
   if (e != hipSuccess) return e;
@@ -202,8 +190,8 @@ struct QKVO {
   void* o;
 };
 
-vggt_status validate_attn(const QKVO& t, vggt_dtype dt, int S, int T, int H, const int32_t* pos, float base,
-                          size_t need_ws, const void* ws, size_t ws_bytes, size_t q_bytes, size_t kv_bytes) {
+vggt_status validate_attn(const QKVO& t, const int32_t* pos, float base, size_t need_ws, const void* ws,
+                          size_t ws_bytes, size_t q_bytes, size_t kv_bytes) {
   if (!t.q || !t.k || !t.v || !t.o) return fail(VGGT_ERR_NULL, "q, k, v and o are required");
   if (!aligned16(t.q) || !aligned16(t.k) || !aligned16(t.v) || !aligned16(t.o))
     return fail(VGGT_ERR_ALIGN, "q/k/v/o must be 16-byte aligned");
@@ -220,12 +208,58 @@ vggt_status validate_attn(const QKVO& t, vggt_dtype dt, int S, int T, int H, con
         overlap(ws, need_ws, t.v, kv_bytes) || overlap(ws, need_ws, t.o, q_bytes))
       return fail(VGGT_ERR_ALIAS, "workspace overlaps a tensor");
   }
-  (void)S; (void)T; (void)H; (void)dt;
   return VGGT_OK;
 }
 
-size_t rope_copy_bytes(int S, int T, int H, vggt_dtype dt) {
-  return align256((size_t)S * T * H * vggt::kHeadDim * elem_size(dt));
+int64_t pad64(int64_t n) { return (n + 63) / 64 * 64; }
+
+// Workspace layout of one attention call.  bf16: RoPE table, rotated K and
+// transposed V for the matrix-core kernel; fp32: rotated copies of Q and K.
+// Both: split partials.  Offsets are 256-byte aligned.
+struct Layout {
+  size_t table = 0, qr = 0, kr = 0, vt = 0, part_o = 0, part_ml = 0, total = 0;
+  bool use_table = false, use_qr = false, use_kr = false, use_vt = false;
+  int64_t vt_pad = 0;   // columns per sequence in V^T
+  int64_t vt_cols = 0;  // total columns of V^T
+  SplitPlan sp{1, 0};
+};
+
+void add(Layout& L, size_t& off, size_t bytes) {
+  off = L.total;
+  L.total += align256(bytes);
+}
+
+// nseq sequences of nq queries and nk keys; q tensor has nseq*nq tokens,
+// k/v tensors nseq*nk tokens; positions repeat every rope_T tokens.
+Layout plan(int nseq, int64_t nq, int64_t nk, int H, int rope_T, bool rope_on, bool allow_split, int kv_splits,
+            vggt_dtype dt) {
+  Layout L;
+  const size_t es = elem_size(dt);
+  const size_t kv_elems = (size_t)nseq * nk * H * vggt::kHeadDim;
+  if (dt == VGGT_BF16) {
+    if (rope_on) {
+      L.use_table = true;
+      add(L, L.table, (size_t)rope_T * 32 * 8);
+      L.use_kr = true;
+      add(L, L.kr, kv_elems * es);
+    }
+    L.use_vt = true;
+    L.vt_pad = pad64(nk);
+    L.vt_cols = (int64_t)nseq * L.vt_pad;
+    add(L, L.vt, (size_t)H * vggt::kHeadDim * L.vt_cols * es);
+  } else if (rope_on) {
+    L.use_qr = true;
+    add(L, L.qr, (size_t)nseq * nq * H * vggt::kHeadDim * es);
+    L.use_kr = true;
+    add(L, L.kr, kv_elems * es);
+  }
+  L.sp = allow_split ? plan_splits(nq, nk, H, kv_splits, dt) : SplitPlan{1, (int)pad64(nk)};
+  if (!allow_split) L.sp.keys_per_split = (int)pad64(nk);
+  if (L.sp.splits > 1) {
+    add(L, L.part_o, (size_t)L.sp.splits * nseq * nq * H * vggt::kHeadDim * 4);
+    add(L, L.part_ml, (size_t)L.sp.splits * nseq * nq * H * 2 * 4);
+  }
+  return L;
 }
 
 vggt::AttnProblem base_problem(const void* q, const void* k, const void* v, void* o, int H, float scale) {
@@ -238,11 +272,54 @@ vggt::AttnProblem base_problem(const void* q, const void* k, const void* v, void
   return p;
 }
 
+// Enqueue the preparation passes and the attention for one call.
+hipError_t run_call(const Layout& L, vggt::AttnProblem p, vggt_dtype dt, int nseq, int64_t nq, int64_t nk,
+                    const int32_t* pos, float base, int rope_T, char* ws, hipStream_t st) {
+  const int H = p.H;
+  hipError_t e = hipSuccess;
+  if (dt == VGGT_BF16) {
+    if (L.use_table) {
+      e = vggt::launch_rope_table(pos, rope_T, (double)base, ws + L.table, st);
+      if (e != hipSuccess) return e;
+      p.rope_tab = (const vggt::f32x2*)(ws + L.table);
+      p.rope_T = rope_T;
+      e = vggt::launch_rope_apply_bf16(p.k, ws + L.kr, (int64_t)nseq * nk, H, rope_T, ws + L.table, st);
+      if (e != hipSuccess) return e;
+      p.k = ws + L.kr;
+    }
+    e = vggt::launch_vt_bf16(p.v, ws + L.vt, nseq, (int)nk, (int)L.vt_pad, H, st);
+    if (e != hipSuccess) return e;
+    p.vt = ws + L.vt;
+    p.vt_cols = L.vt_cols;
+    p.vt_seq_stride = nseq > 1 ? L.vt_pad : 0;
+  } else if (L.use_qr) {
+    e = vggt::launch_rope(p.q, ws + L.qr, false, (int64_t)nseq * nq, rope_T, H, pos, (double)base, st);
+    if (e == hipSuccess) e = vggt::launch_rope(p.k, ws + L.kr, false, (int64_t)nseq * nk, rope_T, H, pos, (double)base, st);
+    if (e != hipSuccess) return e;
+    p.q = ws + L.qr;
+    p.k = ws + L.kr;
+  }
+  p.nq = (int)nq;
+  p.nk = (int)nk;
+  p.nseq = nseq;
+  p.nq_total = (int64_t)nseq * nq;
+  p.q_seq_stride = nseq > 1 ? nq : 0;
+  p.k_seq_stride = nseq > 1 ? nk : 0;
+  p.splits = L.sp.splits;
+  p.keys_per_split = L.sp.keys_per_split;
+  if (L.sp.splits > 1) {
+    p.part_o = (float*)(ws + L.part_o);
+    p.part_ml = (float*)(ws + L.part_ml);
+  }
+  return run_attention(p, dt, st);
+}
+
 }  // namespace
 
 VGGT_API size_t vggt_frame_attn_workspace(int S, int T, int H, int rope_on, vggt_dtype dt) {
   if (!dtype_ok(dt) || !tokens_ok(S, T, H)) return 0;
-  return rope_on ? 2 * rope_copy_bytes(S, T, H, dt) : 0;
+  if (S == 0) return 0;
+  return plan(S, T, T, H, T, rope_on != 0, false, 1, dt).total;
 }
 
 VGGT_API vggt_status vggt_frame_attn(const void* q, const void* k, const void* v, void* o, vggt_dtype dt, int S,
@@ -253,42 +330,21 @@ VGGT_API vggt_status vggt_frame_attn(const void* q, const void* k, const void* v
   if (!tokens_ok(S, T, H)) return fail(VGGT_ERR_SHAPE, "bad shape S=%d T=%d H=%d", S, T, H);
   if (S == 0) return VGGT_OK;
   const size_t bytes = (size_t)S * T * H * vggt::kHeadDim * elem_size(dt);
-  const size_t need = vggt_frame_attn_workspace(S, T, H, pos_yx != nullptr, dt);
-  if (vggt_status s = validate_attn({q, k, v, o}, dt, S, T, H, pos_yx, rope_base, need, workspace, ws_bytes, bytes,
-                                    bytes))
+  const Layout L = plan(S, T, T, H, T, pos_yx != nullptr, false, 1, dt);
+  if (vggt_status s = validate_attn({q, k, v, o}, pos_yx, rope_base, L.total, workspace, ws_bytes, bytes, bytes))
     return s;
   if (vggt_status s = check_device()) return s;
-  hipStream_t st = (hipStream_t)stream;
-  const void *qa = q, *ka = k;
-  if (pos_yx) {
-    char* ws = (char*)workspace;
-    void* qr = ws;
-    void* kr = ws + rope_copy_bytes(S, T, H, dt);
-    hipError_t e = vggt::launch_rope(q, qr, dt == VGGT_BF16, (int64_t)S * T, T, H, pos_yx, rope_base, st);
-    if (e == hipSuccess) e = vggt::launch_rope(k, kr, dt == VGGT_BF16, (int64_t)S * T, T, H, pos_yx, rope_base, st);
-    if (e != hipSuccess) return device_error("rope launch", e);
-    qa = qr;
-    ka = kr;
-  }
-  vggt::AttnProblem p = base_problem(qa, ka, v, o, H, scale);
-  p.q_seq_stride = T;
-  p.k_seq_stride = T;
-  p.nq = T;
-  p.nk = T;
-  p.nseq = S;
-  p.nq_total = (int64_t)S * T;
-  p.splits = 1;
-  p.keys_per_split = ((T + vggt::kAttnKeyTile - 1) / vggt::kAttnKeyTile) * vggt::kAttnKeyTile;
-  hipError_t e = run_attention(p, dt, st);
-  if (e != hipSuccess) return device_error("attention launch", e);
+  hipError_t e = run_call(L, base_problem(q, k, v, o, H, scale), dt, S, T, T, pos_yx, rope_base, T,
+                          (char*)workspace, (hipStream_t)stream);
+  if (e != hipSuccess) return device_error("frame attention launch", e);
   return VGGT_OK;
 }
 
 VGGT_API size_t vggt_global_attn_workspace(int S, int T, int H, int kv_splits, int rope_on, vggt_dtype dt) {
   if (!dtype_ok(dt) || !tokens_ok(S, T, H) || kv_splits < 0 || kv_splits > kMaxSplits) return 0;
+  if (S == 0) return 0;
   const int64_t N = (int64_t)S * T;
-  const SplitPlan sp = plan_splits(N, N, H, kv_splits, dt);
-  return (rope_on ? 2 * rope_copy_bytes(S, T, H, dt) : 0) + partial_bytes(N, H, sp.splits);
+  return plan(1, N, N, H, T, rope_on != 0, true, kv_splits, dt).total;
 }
 
 VGGT_API vggt_status vggt_global_attn(const void* q, const void* k, const void* v, void* o, vggt_dtype dt, int S,
@@ -301,40 +357,13 @@ VGGT_API vggt_status vggt_global_attn(const void* q, const void* k, const void* 
   if (S == 0) return VGGT_OK;
   const int64_t N = (int64_t)S * T;
   const size_t bytes = (size_t)N * H * vggt::kHeadDim * elem_size(dt);
-  const size_t need = vggt_global_attn_workspace(S, T, H, kv_splits, pos_yx != nullptr, dt);
-  if (vggt_status s = validate_attn({q, k, v, o}, dt, S, T, H, pos_yx, rope_base, need, workspace, ws_bytes, bytes,
-                                    bytes))
+  const Layout L = plan(1, N, N, H, T, pos_yx != nullptr, true, kv_splits, dt);
+  if (vggt_status s = validate_attn({q, k, v, o}, pos_yx, rope_base, L.total, workspace, ws_bytes, bytes, bytes))
     return s;
   if (vggt_status s = check_device()) return s;
-  hipStream_t st = (hipStream_t)stream;
-  char* ws = (char*)workspace;
-  const void *qa = q, *ka = k;
-  if (pos_yx) {
-    void* qr = ws;
-    void* kr = ws + rope_copy_bytes(S, T, H, dt);
-    hipError_t e = vggt::launch_rope(q, qr, dt == VGGT_BF16, N, T, H, pos_yx, rope_base, st);
-    if (e == hipSuccess) e = vggt::launch_rope(k, kr, dt == VGGT_BF16, N, T, H, pos_yx, rope_base, st);
-    if (e != hipSuccess) return device_error("rope launch", e);
-    qa = qr;
-    ka = kr;
-    ws += 2 * rope_copy_bytes(S, T, H, dt);
-  }
-  const SplitPlan sp = plan_splits(N, N, H, kv_splits, dt);
-  vggt::AttnProblem p = base_problem(qa, ka, v, o, H, scale);
-  p.q_seq_stride = 0;
-  p.k_seq_stride = 0;
-  p.nq = (int)N;
-  p.nk = (int)N;
-  p.nseq = 1;
-  p.nq_total = N;
-  p.splits = sp.splits;
-  p.keys_per_split = sp.keys_per_split;
-  if (sp.splits > 1) {
-    p.part_o = (float*)ws;
-    p.part_ml = (float*)(ws + align256((size_t)sp.splits * N * H * vggt::kHeadDim * 4));
-  }
-  hipError_t e = run_attention(p, dt, st);
-  if (e != hipSuccess) return device_error("attention launch", e);
+  hipError_t e = run_call(L, base_problem(q, k, v, o, H, scale), dt, 1, N, N, pos_yx, rope_base, T,
+                          (char*)workspace, (hipStream_t)stream);
+  if (e != hipSuccess) return device_error("global attention launch", e);
   return VGGT_OK;
 }
 
@@ -376,9 +405,8 @@ VGGT_API size_t vggt_descriptor_xattn_workspace(int S, int T, int Dn, int H, int
   if (!dtype_ok(dt) || !tokens_ok(S, T, H) || Dn < 1 || !tokens_ok(S, Dn, H) || kv_splits < 0 ||
       kv_splits > kMaxSplits)
     return 0;
-  const int64_t nq = (int64_t)S * T, nk = (int64_t)S * Dn;
-  const SplitPlan sp = plan_splits(nq, nk, H, kv_splits, dt);
-  return partial_bytes(nq, H, sp.splits);
+  if (S == 0) return 0;
+  return plan(1, (int64_t)S * T, (int64_t)S * Dn, H, 1, false, true, kv_splits, dt).total;
 }
 
 VGGT_API vggt_status vggt_descriptor_xattn(const void* q, const void* kd, const void* vd, void* o, vggt_dtype dt,
@@ -393,24 +421,12 @@ VGGT_API vggt_status vggt_descriptor_xattn(const void* q, const void* kd, const 
   const int64_t nq = (int64_t)S * T, nk = (int64_t)S * Dn;
   const size_t q_b = (size_t)nq * H * vggt::kHeadDim * elem_size(dt);
   const size_t kv_b = (size_t)nk * H * vggt::kHeadDim * elem_size(dt);
-  const size_t need = vggt_descriptor_xattn_workspace(S, T, Dn, H, kv_splits, dt);
-  if (vggt_status s = validate_attn({q, kd, vd, o}, dt, S, T, H, nullptr, 0.0f, need, workspace, ws_bytes, q_b, kv_b))
+  const Layout L = plan(1, nq, nk, H, 1, false, true, kv_splits, dt);
+  if (vggt_status s = validate_attn({q, kd, vd, o}, nullptr, 0.0f, L.total, workspace, ws_bytes, q_b, kv_b))
     return s;
   if (vggt_status s = check_device()) return s;
-  const SplitPlan sp = plan_splits(nq, nk, H, kv_splits, dt);
-  vggt::AttnProblem p = base_problem(q, kd, vd, o, H, scale);
-  p.nq = (int)nq;
-  p.nk = (int)nk;
-  p.nseq = 1;
-  p.nq_total = nq;
-  p.splits = sp.splits;
-  p.keys_per_split = sp.keys_per_split;
-  if (sp.splits > 1) {
-    char* ws = (char*)workspace;
-    p.part_o = (float*)ws;
-    p.part_ml = (float*)(ws + align256((size_t)sp.splits * nq * H * vggt::kHeadDim * 4));
-  }
-  hipError_t e = run_attention(p, dt, (hipStream_t)stream);
-  if (e != hipSuccess) return device_error("attention launch", e);
+  hipError_t e = run_call(L, base_problem(q, kd, vd, o, H, scale), dt, 1, nq, nk, nullptr, 0.0f, 1,
+                          (char*)workspace, (hipStream_t)stream);
+  if (e != hipSuccess) return device_error("descriptor attention launch", e);
   return VGGT_OK;
 }
