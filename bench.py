@@ -46,6 +46,8 @@ def main() -> int:
     ap.add_argument("--workload", default="vggt-518-s32")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-row-stride", type=int, default=48)
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB first (hardware-counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -101,6 +103,15 @@ def main() -> int:
         mark(3)
         ffv.vggt_descriptor_xattn(qd, kpool, vpool, out=xo, kv_splits=0, workspace=ws_x)
         mark(4)
+
+    if args.calibrate_copy_mib > 0:
+        n = args.calibrate_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         step()

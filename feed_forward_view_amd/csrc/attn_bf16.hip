@@ -6,36 +6,45 @@
 // sum against a reference offset, so a row costs O(1) memory for any key
 // count.
 //
-// Work split.  A workgroup of 4 waves owns 256 queries of one head; each wave
-// owns 64 of them (two 32-query MFMA column blocks).  Per 64-key tile:
-//   S^T = K Q^T   16 x v_mfma_f32_32x32x16_bf16 (keys are the M dimension, so
-//                 one lane holds 32 scores of a single query);
-//   P = 2^(S^T - m) in fp32, rounded to bf16; the row sum adds the rounded
-//                 P pairs with v_dot2_f32_bf16, i.e. exactly the weights the
-//                 P V product uses;
-//   O^T += V^T P^T  16 x v_mfma_f32_32x32x16_bf16 (head dim is M, the lane
-//                 again holds one query, so per-row scaling stays in-lane).
+// Work split.  A workgroup of 4 waves (one per SIMD) owns 256 queries of one
+// head; each wave owns 64 of them (two 32-query MFMA column blocks, qb).  Per
+// 64-key tile:
+//   S^T = K Q^T - m   16 x v_mfma_f32_32x32x16_bf16; keys are the M dimension
+//                     so one lane holds 32 scores of a single query, and the
+//                     row reference m enters through the accumulator input;
+//   P = 2^(S^T)       one v_exp_f32 per score, rounded to bf16 in pairs; the
+//                     row sum adds the rounded pairs with v_dot2_f32_bf16, so
+//                     it uses exactly the weights of the P V product;
+//   O^T += V^T P^T    16 x v_mfma_f32_32x32x16_bf16; head dim is M and the lane
+//                     again holds one query, so per-row scaling stays in-lane.
 // Q is rotated (2D RoPE, fp32, from the per-position cos/sin table) and
-// multiplied by scale*log2(e) once in the prologue, so scores come out of the
-// MFMA in log2 units.  The score-tile rows are taken in the key order rho
-// (bits 2 and 3 of the key index swapped) so that the S^T accumulator
-// registers are, in order, exactly the bf16 B operand of the P V product.
+// multiplied by scale*log2(e) once in the prologue, so scores come out in log2
+// units.  The score-tile rows are taken in the key order rho (bits 2 and 3 of
+// the key index swapped) so that the S^T accumulator registers are, in order,
+// exactly the bf16 B operand of the P V product.
 //
-// Softmax reference.  The reference m of a row starts at 0 and is left there
-// while the row's scores stay within 2^32 of it: then 2^s needs no subtraction
-// at all, and each score costs one v_exp_f32, half a v_cvt_pk_bf16_f32 and
-// half a v_dot2.  The first tile, and any tile whose partial row sum leaves
-// [0, 2^64], takes a slow path that computes the tile maximum, moves m
-// (rescaling O and the sum exactly by 2^(m_old - m_new)) and redoes the
-// tile; from then on the wave subtracts m before the exponential.  The final
-// O / l is the same softmax whatever m is.
+// Overlap.  On gfx950 the exponentials (transcendental unit) can issue
+// while an MFMA of the same SIMD executes, but ordinary vector ALU work
+// cannot, so the loop keeps non-exponential VALU work per tile to the
+// minimum (one cvt and one dot2 per score pair) and interleaves each query
+// block's exponentials with the other block's MFMAs; two waves per SIMD
+// supply the rest of the overlap.
 //
-// Operands.  K rows (rotated by a pre-pass when RoPE is on) and V^T rows
-// (transposed by a pre-pass, every sequence starting at a multiple of 64
-// columns) are copied straight from global memory into LDS with
-// global_load_lds_dwordx4, 16-byte units XOR-swizzled per row so that the
-// 16-byte MFMA operand reads are free of bank conflicts; two stages, one
-// barrier per tile.  Keys past the end of a range are masked to -inf.
+// Softmax reference.  m starts at 0 and stays there while a row's scores stay
+// within 2^32 of it.  The first tile, and any tile whose partial row sum
+// leaves [0, 2^64], takes a slow path that computes the tile maximum, moves m
+// (rescaling O and the running sum exactly by 2^(m_old - m_new)) and redoes
+// the tile; from then on the wave subtracts m before the exponential.  The
+// final O / l is the same softmax whatever m is.
+//
+// Operands.  A pre-pass lays K (rotated when RoPE is on) and V^T out in
+// tiles of 64 keys, each tile 8 KiB in exactly the order the LDS tile uses
+// (rows in the key order rho, 16-byte units XOR-swizzled per row so the
+// 16-byte MFMA operand reads are free of bank conflicts; keys past the end
+// are zero).  Tiles are then copied linearly into a 4-stage LDS ring with
+// global_load_lds_dwordx4, three tiles ahead of use; one barrier per tile.
+// The last (partial) tile of a key range is peeled out of the loop and its
+// missing keys are masked to -inf.
 //
 // Workgroup order is XCD-aware: the hardware deals workgroups round-robin to
 // the 8 XCDs, so the linear id is remapped to give each XCD a contiguous run
@@ -51,6 +60,7 @@ constexpr int BK = kAttnKeyTile;  // 64 keys per tile
 constexpr int NW = 4;             // waves per workgroup
 constexpr int NT = NW * 64;
 constexpr int BQ = NW * 64;       // 64 queries per wave
+constexpr int NSTAGE = 4;         // LDS ring depth (tiles in flight = NSTAGE - 1)
 constexpr float kSumLimit = 18446744073709551616.0f;  // 2^64
 constexpr float kRaise = 32.0f;   // move m when a tile max exceeds it by this
 constexpr float kLow = -64.0f;    // first tile: move m down when the max is below this
@@ -63,8 +73,8 @@ typedef __attribute__((address_space(3))) void lds_void;
 // K tile:   row r holds key rho(r) of the tile, 8 units of 8 dims; unit u at slot u ^ (r & 7).
 // V^T tile: row d holds channel d of the 64 keys; unit u (keys 8u..8u+7) at slot u ^ vt_swz(d).
 struct Smem {
-  u32x4 k[2][BK][8];
-  u32x4 vt[2][D][8];
+  u32x4 k[NSTAGE][BK][8];
+  u32x4 vt[NSTAGE][D][8];
 };
 
 __device__ __forceinline__ void xcd_remap(int w, int nwg, int& logical) {
@@ -77,6 +87,24 @@ __device__ __forceinline__ float dot2_acc(uint32_t pk, float acc) {
   const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), one, acc, false);
 }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+}
+
+// interleave hint for the scheduler: n x (1 MFMA, v VALU)
+#define VGGT_INTERLEAVE(n, v)                                  \
+  _Pragma("unroll") for (int _i = 0; _i < (n); ++_i) {         \
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         \
+    __builtin_amdgcn_sched_group_barrier(0x002, (v), 0);       \
+  }
+
+struct Tile {
+  f32x16 s[2][2];  // [kb][qb]
+};
 
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_bf16_kernel(AttnProblem p) {
@@ -100,8 +128,9 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
   const int seq = rest / p.splits;
 
   const uint16_t* __restrict__ qg = (const uint16_t*)p.q + (seq * p.q_seq_stride) * p.tok_stride + head * D;
-  const uint16_t* __restrict__ kg = (const uint16_t*)p.k + (seq * p.k_seq_stride) * p.tok_stride + head * D;
-  const uint16_t* __restrict__ vtg = (const uint16_t*)p.vt + (int64_t)head * D * p.vt_cols + seq * p.vt_seq_stride;
+  // K and V^T tiles of this (sequence, head): 512 16-byte units per tile
+  const u32x4* __restrict__ ktg = (const u32x4*)p.k + ((int64_t)seq * p.H + head) * p.ktiles_seq * 512;
+  const u32x4* __restrict__ vtg = (const u32x4*)p.vt + ((int64_t)seq * p.H + head) * p.ktiles_seq * 512;
 
   const int kbeg = split * p.keys_per_split;
   const int kend = min(p.nk, kbeg + p.keys_per_split);
@@ -110,49 +139,60 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
   const int q0 = qt * BQ + wave * 64;  // first query of this wave
   const bool active = q0 < p.nq;
 
-  // ---- tile loads: each wave moves two 1 KiB blocks of K and two of V^T
-  auto issue = [&](int stage, int kt) {
+  // ---- tile loads: each wave copies two 1 KiB blocks of the K tile and two of the V^T tile
+  const int ktile0 = kbeg / BK;
+  auto issue = [&](int stage, int tile) {
+    const u32x4* ks = ktg + (int64_t)(ktile0 + tile) * 512 + wave * 128 + lane;
+    const u32x4* vs = vtg + (int64_t)(ktile0 + tile) * 512 + wave * 128 + lane;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      const int blk = 2 * wave + c;
-      const int r = blk * 8 + (lane >> 3);
-      const int s = lane & 7;
-      const int key = min(kt + rho(r), kend - 1);
-      const uint16_t* ksrc = kg + (int64_t)key * p.tok_stride + 8 * (s ^ (r & 7));
-      __builtin_amdgcn_global_load_lds((const void*)ksrc, (lds_void*)&sm.k[stage][blk * 8][0], 16, 0, 0);
-      const uint16_t* vsrc = vtg + (int64_t)r * p.vt_cols + kt + 8 * (s ^ vt_swz(r));
-      __builtin_amdgcn_global_load_lds((const void*)vsrc, (lds_void*)&sm.vt[stage][blk * 8][0], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(ks + 64 * c), (lds_void*)&sm.k[stage][(2 * wave + c) * 8][0], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(vs + 64 * c), (lds_void*)&sm.vt[stage][(2 * wave + c) * 8][0], 16, 0, 0);
     }
   };
 
-  issue(0, kbeg);
+#pragma unroll
+  for (int i = 0; i < NSTAGE - 1; ++i)
+    if (i < ntiles) issue(i, i);
 
   // ---- Q fragments (B operand of S^T = K Q^T): lane holds query q0+32*qb+l32,
   //      dims 16*dc + 8*hi .. +7, rotated and scaled by scale*log2(e).
   bf16x8 qf[2][4];
+  {
+    const f32x2* __restrict__ tab = p.rope_tab;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int qi = q0 + 32 * qb + l32;
-    const bool ok = qi < p.nq;
-    const int tpos = p.rope_tab ? (int)((seq * p.q_seq_stride + qi) % p.rope_T) : 0;
+    for (int qb = 0; qb < 2; ++qb) {
+      const int qi = q0 + 32 * qb + l32;
+      const bool ok = qi < p.nq;
+      const int qrow = ok ? qi : 0;
+      const int tpos = tab ? (int)((seq * p.q_seq_stride + qrow) % p.rope_T) : 0;
+      const f32x2* trow = tab ? tab + tpos * 32 + 4 * hi : nullptr;
 #pragma unroll
-    for (int dc = 0; dc < 4; ++dc) {
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (ok) w = *(const u32x4*)(qg + (int64_t)qi * p.tok_stride + 16 * dc + 8 * hi);
-      u32x4 r;
+      for (int dc = 0; dc < 4; ++dc) {
+        u32x4 w = *(const u32x4*)(qg + (int64_t)qrow * p.tok_stride + 16 * dc + 8 * hi);
+        if (!ok) w = u32x4{0u, 0u, 0u, 0u};
+        float x[4], y[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float x = lo_bf16(w[e]), y = hi_bf16(w[e]);
-        if (p.rope_tab && ok) {
-          const f32x2 cs = p.rope_tab[tpos * 32 + 8 * dc + 4 * hi + e];
-          const float x2 = __builtin_fmaf(x, cs[0], -y * cs[1]);
-          const float y2 = __builtin_fmaf(x, cs[1], y * cs[0]);
-          x = x2;
-          y = y2;
+        for (int e = 0; e < 4; ++e) {
+          x[e] = lo_bf16(w[e]);
+          y[e] = hi_bf16(w[e]);
         }
-        r[e] = pack_bf16x2(x * p.scale_log2, y * p.scale_log2);
+        if (trow) {
+          // pairs 8*dc + 4*hi + e of the 32 rotation pairs of this position
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const f32x2 cs = trow[8 * dc + e];
+            const float x2 = __builtin_fmaf(x[e], cs[0], -y[e] * cs[1]);
+            const float y2 = __builtin_fmaf(x[e], cs[1], y[e] * cs[0]);
+            x[e] = x2;
+            y[e] = y2;
+          }
+        }
+        u32x4 r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[e] = pack_bf16x2(x[e] * p.scale_log2, y[e] * p.scale_log2);
+        qf[qb][dc] = __builtin_bit_cast(bf16x8, r);
       }
-      qf[qb][dc] = __builtin_bit_cast(bf16x8, r);
     }
   }
 
@@ -168,136 +208,174 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
   float lsum[2] = {0.0f, 0.0f};  // this lane's partial row sums
   bool offs = false;             // some row of the wave has m != 0
 
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
+  f32x16 s0[2], s1[2];       // [kb] scores of query blocks 0 and 1
+  uint32_t p0[2][2][4], p1[2][2][4];
+  bf16x8 kf[2][4];           // K fragments of the tile
+  bf16x8 vf[2][2][2];        // V^T fragments [kb][j][db]
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    const int kt = kbeg + t * BK;
-    if (t + 1 < ntiles) issue(buf ^ 1, kt + BK);
-
-    if (active) {
-      // S^T = K Q^T for two 32-key blocks
-      f32x16 s[2][2];
+  auto read_k = [&](int stage) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int row = 32 * kb + l32;
+    for (int kb = 0; kb < 2; ++kb) {
+      const int row = 32 * kb + l32;
 #pragma unroll
-        for (int dc = 0; dc < 4; ++dc) {
-          const int u = 2 * dc + hi;
-          const bf16x8 kf = __builtin_bit_cast(bf16x8, sm.k[buf][row][u ^ (row & 7)]);
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb) {
-            if (dc == 0) {
-              const f32x16 z = {};
-              s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][0], z, 0, 0, 0);
-            } else {
-              s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][dc], s[kb][qb], 0, 0, 0);
-            }
-          }
-        }
+      for (int dc = 0; dc < 4; ++dc) {
+        const int u = 2 * dc + hi;
+        kf[kb][dc] = __builtin_bit_cast(bf16x8, sm.k[stage][row][u ^ (row & 7)]);
       }
-      // mask keys past the end (only the last tile of a range has them);
-      // lane/reg -> key kt + 32*kb + 16*(r/8) + 8*hi + r%8
-      if (kt + BK > kend) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kt + 32 * kb + 16 * (r >> 3) + 8 * hi + (r & 7);
-            if (key >= kend) {
-              s[kb][0][r] = -INFINITY;
-              s[kb][1][r] = -INFINITY;
-            }
-          }
-      }
-      // P = 2^(S - m) as bf16 pairs; tile partial row sums
-      uint32_t pf[2][2][2][4];  // [qb][kb][j] bf16 pairs of keys 32kb+16j+8hi+0..7
-      float ls[2];
-      auto exps = [&](bool sub) {
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          float acc = 0.0f;
-          const float m = sub ? mref[qb] : 0.0f;
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                float a = s[kb][qb][8 * j + 2 * e], b = s[kb][qb][8 * j + 2 * e + 1];
-                if (sub) {
-                  a -= m;
-                  b -= m;
-                }
-                const uint32_t w = pack_bf16x2(__builtin_amdgcn_exp2f(a), __builtin_amdgcn_exp2f(b));
-                pf[qb][kb][j][e] = w;
-                acc = dot2_acc(w, acc);
-              }
-          ls[qb] = acc;
-        }
-      };
-      if (offs)
-        exps(true);
-      else
-        exps(false);
-      const bool bad = !(ls[0] <= kSumLimit) || !(ls[1] <= kSumLimit);
-      if (t == 0 || __any(bad)) {
-        // slow path: move the reference where needed, then redo the tile
-        bool any_m = false;
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          float mx = s[0][qb][0];
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
-          mx = fmaxf(mx, __shfl_xor(mx, 32));
-          float mnew = mref[qb];
-          if (t == 0) {
-            if (mx < kLow || mx > kRaise) mnew = mx;
-          } else if (mx - mref[qb] > kRaise) {
-            mnew = mx;
-          }
-          if (mnew != mref[qb]) {
-            const float alpha = __builtin_amdgcn_exp2f(mref[qb] - mnew);
-            lsum[qb] *= alpha;
-#pragma unroll
-            for (int db = 0; db < 2; ++db)
-#pragma unroll
-              for (int r = 0; r < 16; ++r) o[db][qb][r] *= alpha;
-            mref[qb] = mnew;
-          }
-          any_m = any_m || (mref[qb] != 0.0f);
-        }
-        offs = __any(any_m);
-        exps(true);
-      }
-      lsum[0] += ls[0];
-      lsum[1] += ls[1];
-      // O^T += V^T P^T
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int u = 4 * kb + 2 * j + hi;
-#pragma unroll
-          for (int db = 0; db < 2; ++db) {
-            const int d = 32 * db + l32;
-            const bf16x8 vf = __builtin_bit_cast(bf16x8, sm.vt[buf][d][u ^ vt_swz(d)]);
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-              const u32x4 w = {pf[qb][kb][j][0], pf[qb][kb][j][1], pf[qb][kb][j][2], pf[qb][kb][j][3]};
-              o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, __builtin_bit_cast(bf16x8, w), o[db][qb], 0, 0, 0);
-            }
-          }
-        }
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-  }
+  };
+  auto read_v = [&](int stage) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int u = 4 * kb + 2 * j + hi;
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+          const int d = 32 * db + l32;
+          vf[kb][j][db] = __builtin_bit_cast(bf16x8, sm.vt[stage][d][u ^ vt_swz(d)]);
+        }
+      }
+  };
+  auto qk = [&](f32x16 (&s)[2], int qb) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const f32x16 z = {};
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb][0], qf[qb][0], z, 0, 0, 0);
+#pragma unroll
+      for (int dc = 1; dc < 4; ++dc)
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb][dc], qf[qb][dc], s[kb], 0, 0, 0);
+    }
+  };
+  auto pv = [&](const uint32_t (&pf)[2][2][4], int qb) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const u32x4 w = {pf[kb][j][0], pf[kb][j][1], pf[kb][j][2], pf[kb][j][3]};
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+          o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kb][j][db], __builtin_bit_cast(bf16x8, w),
+                                                              o[db][qb], 0, 0, 0);
+      }
+  };
+  // P = 2^(S - m) as bf16 pairs of keys 32kb+16j+8hi+0..7; returns the partial row sum
+  auto soft = [&](const f32x16 (&s)[2], bool sub, float m, uint32_t (&pf)[2][2][4]) -> float {
+    float acc = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float a = s[kb][8 * j + 2 * e], b = s[kb][8 * j + 2 * e + 1];
+          if (sub) {
+            a -= m;
+            b -= m;
+          }
+          const uint32_t w = pack_bf16x2(__builtin_amdgcn_exp2f(a), __builtin_amdgcn_exp2f(b));
+          pf[kb][j][e] = w;
+          acc = dot2_acc(w, acc);
+        }
+    return acc;
+  };
+  // slow path of one unit: move the reference if needed and redo its exponentials
+  auto slow = [&](const f32x16 (&s)[2], int qb, bool first, uint32_t (&pf)[2][2][4]) -> float {
+    float mx = s[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    float mnew = mref[qb];
+    if (first) {
+      if (mx < kLow || mx > kRaise) mnew = mx;
+    } else if (mx - mref[qb] > kRaise) {
+      mnew = mx;
+    }
+    if (__any(mnew != mref[qb])) {
+      const float alpha = __builtin_amdgcn_exp2f(mref[qb] - mnew);
+      lsum[qb] *= alpha;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        o[0][qb][r] *= alpha;
+        o[1][qb][r] *= alpha;
+      }
+      mref[qb] = mnew;
+      offs = __any(mref[0] != 0.0f || mref[1] != 0.0f);
+    }
+    return soft(s, true, mref[qb], pf);
+  };
+  auto mask = [&](f32x16 (&s)[2], int kt) {
+    // lane/reg -> key kt + 32*kb + 16*(r/8) + 8*hi + r%8
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (kt + 32 * kb + 16 * (r >> 3) + 8 * hi + (r & 7) >= kend) s[kb][r] = -INFINITY;
+  };
 
-  if (!active) return;
+  // wait until tile `tile` has landed in LDS (later tiles may still be in flight), then barrier
+  auto land = [&](int tile) {
+    const int ahead = min(NSTAGE - 2, ntiles - 1 - tile);  // tiles issued after `tile`
+    if (ahead >= 2)
+      wait_vmcnt<8>();
+    else if (ahead == 1)
+      wait_vmcnt<4>();
+    else
+      wait_vmcnt<0>();
+    __syncthreads();
+  };
+
+  // one tile: S^T of block 1 || exp of block 0, then P V of block 0 || exp of block 1
+  auto tile_body = [&](int t, bool masked) {
+    const int stage = t % NSTAGE;
+    const bool first = t == 0;
+    read_k(stage);
+    qk(s0, 0);
+    if (masked) mask(s0, kbeg + t * BK);
+    float ls0, ls1;
+    if (offs) {
+      qk(s1, 1);
+      ls0 = soft(s0, true, mref[0], p0);
+    } else {
+      qk(s1, 1);
+      ls0 = soft(s0, false, 0.0f, p0);
+      VGGT_INTERLEAVE(8, 8);
+    }
+    if (masked) mask(s1, kbeg + t * BK);
+    if (first || __any(!(ls0 <= kSumLimit))) ls0 = slow(s0, 0, first, p0);
+    lsum[0] += ls0;
+    read_v(stage);
+    if (offs) {
+      pv(p0, 0);
+      ls1 = soft(s1, true, mref[1], p1);
+    } else {
+      pv(p0, 0);
+      ls1 = soft(s1, false, 0.0f, p1);
+      VGGT_INTERLEAVE(8, 8);
+    }
+    if (first || __any(!(ls1 <= kSumLimit))) ls1 = slow(s1, 1, first, p1);
+    lsum[1] += ls1;
+    pv(p1, 1);
+  };
+
+  if (active) {
+    for (int t = 0; t + 1 < ntiles; ++t) {
+      land(t);
+      if (t + NSTAGE - 1 < ntiles) issue((t + NSTAGE - 1) % NSTAGE, t + NSTAGE - 1);
+      tile_body(t, false);
+    }
+    land(ntiles - 1);
+    tile_body(ntiles - 1, kbeg + ntiles * BK > kend);
+  } else {
+    // keep the workgroup's barrier and load sequence
+    for (int t = 0; t < ntiles; ++t) {
+      land(t);
+      if (t + NSTAGE - 1 < ntiles) issue((t + NSTAGE - 1) % NSTAGE, t + NSTAGE - 1);
+    }
+    return;
+  }
 
   // ---- epilogue
 #pragma unroll

@@ -32,7 +32,7 @@ constexpr int kMaxHeads = 128;
 constexpr int64_t kMaxTokens = int64_t(1) << 28;
 constexpr int kMaxSplits = 64;
 constexpr int kAssumedCUs = 256;       // MI355X; used only to size the key split
-constexpr int kWorkgroupsPerCU = 2;
+constexpr int kWorkgroupsPerCU = 1;  // the bf16 kernel runs one 4-wave workgroup per CU
 
 // ---- device check, cached per device (read-only after first use)
 struct DevInfo {
@@ -217,10 +217,9 @@ int64_t pad64(int64_t n) { return (n + 63) / 64 * 64; }
 // transposed V for the matrix-core kernel; fp32: rotated copies of Q and K.
 // Both: split partials.  Offsets are 256-byte aligned.
 struct Layout {
-  size_t table = 0, qr = 0, kr = 0, vt = 0, part_o = 0, part_ml = 0, total = 0;
-  bool use_table = false, use_qr = false, use_kr = false, use_vt = false;
-  int64_t vt_pad = 0;   // columns per sequence in V^T
-  int64_t vt_cols = 0;  // total columns of V^T
+  size_t table = 0, qr = 0, kr = 0, kt = 0, vt = 0, part_o = 0, part_ml = 0, total = 0;
+  bool use_table = false, use_qr = false, use_kr = false;
+  int ktiles = 0;  // bf16: key tiles of 64 per sequence
   SplitPlan sp{1, 0};
 };
 
@@ -231,30 +230,28 @@ void add(Layout& L, size_t& off, size_t bytes) {
 
 // nseq sequences of nq queries and nk keys; q tensor has nseq*nq tokens,
 // k/v tensors nseq*nk tokens; positions repeat every rope_T tokens.
+// bf16: RoPE table plus K and V^T in 64-key tile layout; fp32: rotated copies
+// of Q and K.  Both: split partials.  Offsets are 256-byte aligned.
 Layout plan(int nseq, int64_t nq, int64_t nk, int H, int rope_T, bool rope_on, bool allow_split, int kv_splits,
             vggt_dtype dt) {
   Layout L;
   const size_t es = elem_size(dt);
-  const size_t kv_elems = (size_t)nseq * nk * H * vggt::kHeadDim;
   if (dt == VGGT_BF16) {
     if (rope_on) {
       L.use_table = true;
       add(L, L.table, (size_t)rope_T * 32 * 8);
-      L.use_kr = true;
-      add(L, L.kr, kv_elems * es);
     }
-    L.use_vt = true;
-    L.vt_pad = pad64(nk);
-    L.vt_cols = (int64_t)nseq * L.vt_pad;
-    add(L, L.vt, (size_t)H * vggt::kHeadDim * L.vt_cols * es);
+    L.ktiles = (int)((nk + 63) / 64);
+    const size_t tiles_bytes = (size_t)nseq * H * L.ktiles * 64 * vggt::kHeadDim * 2;
+    add(L, L.kt, tiles_bytes);
+    add(L, L.vt, tiles_bytes);
   } else if (rope_on) {
     L.use_qr = true;
     add(L, L.qr, (size_t)nseq * nq * H * vggt::kHeadDim * es);
     L.use_kr = true;
-    add(L, L.kr, kv_elems * es);
+    add(L, L.kr, (size_t)nseq * nk * H * vggt::kHeadDim * es);
   }
   L.sp = allow_split ? plan_splits(nq, nk, H, kv_splits, dt) : SplitPlan{1, (int)pad64(nk)};
-  if (!allow_split) L.sp.keys_per_split = (int)pad64(nk);
   if (L.sp.splits > 1) {
     add(L, L.part_o, (size_t)L.sp.splits * nseq * nq * H * vggt::kHeadDim * 4);
     add(L, L.part_ml, (size_t)L.sp.splits * nseq * nq * H * 2 * 4);
@@ -278,20 +275,20 @@ hipError_t run_call(const Layout& L, vggt::AttnProblem p, vggt_dtype dt, int nse
   const int H = p.H;
   hipError_t e = hipSuccess;
   if (dt == VGGT_BF16) {
+    const void* table = nullptr;
     if (L.use_table) {
       e = vggt::launch_rope_table(pos, rope_T, (double)base, ws + L.table, st);
       if (e != hipSuccess) return e;
-      p.rope_tab = (const vggt::f32x2*)(ws + L.table);
+      table = ws + L.table;
+      p.rope_tab = (const vggt::f32x2*)table;
       p.rope_T = rope_T;
-      e = vggt::launch_rope_apply_bf16(p.k, ws + L.kr, (int64_t)nseq * nk, H, rope_T, ws + L.table, st);
-      if (e != hipSuccess) return e;
-      p.k = ws + L.kr;
     }
-    e = vggt::launch_vt_bf16(p.v, ws + L.vt, nseq, (int)nk, (int)L.vt_pad, H, st);
+    e = vggt::launch_k_tiles_bf16(p.k, ws + L.kt, nseq, (int)nk, H, table, rope_T, st);
+    if (e == hipSuccess) e = vggt::launch_v_tiles_bf16(p.v, ws + L.vt, nseq, (int)nk, H, st);
     if (e != hipSuccess) return e;
+    p.k = ws + L.kt;
     p.vt = ws + L.vt;
-    p.vt_cols = L.vt_cols;
-    p.vt_seq_stride = nseq > 1 ? L.vt_pad : 0;
+    p.ktiles_seq = L.ktiles;
   } else if (L.use_qr) {
     e = vggt::launch_rope(p.q, ws + L.qr, false, (int64_t)nseq * nq, rope_T, H, pos, (double)base, st);
     if (e == hipSuccess) e = vggt::launch_rope(p.k, ws + L.kr, false, (int64_t)nseq * nk, rope_T, H, pos, (double)base, st);

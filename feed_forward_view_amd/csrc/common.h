@@ -37,10 +37,9 @@ struct AttnProblem {
   const void* q;
   const void* k;
   const void* v;           // V [tokens][H][64] (fp32 kernel)
-  const void* vt;          // V^T [H][64][vt_cols] (bf16 kernel)
+  const void* vt;          // bf16 kernel: V^T tiles [nseq][H][ntile][64][64]; K is in p.k as K tiles
+  int ktiles_seq;          // bf16 kernel: key tiles per sequence in the tile layouts
   const f32x2* rope_tab;   // [rope_T][32] (cos, sin) applied to Q in the bf16 kernel, or null
-  int64_t vt_cols;         // row length of V^T
-  int64_t vt_seq_stride;   // V^T column of key 0 of sequence s is s * vt_seq_stride
   int rope_T;              // token positions repeat every rope_T tokens
   void* o;                 // final output (dtype of the call)
   float* part_o;           // [splits][nq_total][H][64]
@@ -66,9 +65,9 @@ hipError_t launch_attn_merge(const AttnProblem& p, bool out_bf16, hipStream_t st
 hipError_t launch_rope(const void* src, void* dst, bool bf16, int64_t n_tok, int T, int H, const int32_t* pos_yx,
                        double base, hipStream_t stream);
 hipError_t launch_rope_table(const int32_t* pos_yx, int T, double base, void* table, hipStream_t stream);
-hipError_t launch_rope_apply_bf16(const void* src, void* dst, int64_t n_tok, int H, int T, const void* table,
-                                  hipStream_t stream);
-hipError_t launch_vt_bf16(const void* v, void* vt, int nseq, int len, int pad, int H, hipStream_t stream);
+hipError_t launch_k_tiles_bf16(const void* k, void* kt, int nseq, int len, int H, const void* table, int rope_T,
+                               hipStream_t stream);
+hipError_t launch_v_tiles_bf16(const void* v, void* vt, int nseq, int len, int H, hipStream_t stream);
 hipError_t launch_pool(const void* k, const void* v, void* kd, void* vd, bool bf16, int S, int T, int H, int gh,
                        int gw, int patch_begin, int ph, int pw, int Dn, hipStream_t stream);
 

@@ -1,4 +1,4 @@
-// Operand preparation for the bf16 attention kernel (all HBM-bound, one pass).
+// Operand preparation for the bf16 attention kernel (HBM-bound passes).
 //
 //  rope_table_kernel  cos/sin of the 32 rotation angles of every in-frame
 //                     position: table[t][k], k < 16 turns with the row and
@@ -7,13 +7,11 @@
 //                     of the "VGGT 論文報告" slide deck, Section IV, slide
 //                     4/6, per axis; rope_base of the VGGT-Omega-1B-512-bf16
 //                     config article).
-//  rope_apply_kernel  rotated copy of K (bf16) using the table; a pair whose
-//                     angle is 0 is copied unchanged.
-//  vt_kernel          V [seq][len][H][64] -> V^T [H][64][nseq * pad]: for each
-//                     head and channel, the keys of a sequence are contiguous
-//                     and every sequence starts at a multiple of 64 columns
-//                     (pad columns are zero), so the attention kernel can
-//                     stream 16-byte key units of V^T straight into LDS.
+//  k_tiles_kernel     K -> 64-key tiles in the attention kernel's LDS order,
+//                     rotated by the table when RoPE is on.
+//  v_tiles_kernel     V -> 64-key tiles of V^T in the attention kernel's LDS
+//                     order.
+// Each tile is 8 KiB and the attention kernel copies it linearly into LDS.
 #include "common.h"
 
 namespace vggt {
@@ -30,61 +28,78 @@ __global__ __launch_bounds__(NT) void rope_table_kernel(const int32_t* __restric
   table[i] = f32x2{(float)cos(theta), (float)sin(theta)};
 }
 
-// one thread per 16-byte unit (8 bf16 = 4 rotation pairs)
-__global__ __launch_bounds__(NT) void rope_apply_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
-                                                        int64_t n_units, int H, int T,
-                                                        const f32x2* __restrict__ table) {
-  const int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x;
-  if (i >= n_units) return;
-  const int u = (int)(i & 7);                // unit within a head row
-  const int64_t tok = i / (8 * (int64_t)H);
-  const int t = (int)(tok % T);
-  const u32x4 w = src[i];
-  u32x4 r;
+__device__ __forceinline__ int rho_key(int i) { return (i & ~0xC) | ((i & 4) << 1) | ((i & 8) >> 1); }
+__device__ __forceinline__ int swz_vt(int d) { return (d ^ (d >> 3)) & 7; }
+
+// K [nseq*len][H][64] -> KT [nseq][H][ntile][64 rows][8 slots of 16 bytes]: row r of tile
+// kt holds key 64*kt + rho(r), slot s holds its channels 8u..8u+7 with u = s ^ (r & 7); keys
+// past len are zero.  With a table, pairs are rotated as in rope_apply_kernel (the
+// position of key j of sequence q is (q*len + j) % rope_T).  grid (ntile, H, nseq).
+__global__ __launch_bounds__(NT) void k_tiles_kernel(const uint16_t* __restrict__ k, u32x4* __restrict__ kt_out,
+                                                     int len, int H, const f32x2* __restrict__ table, int rope_T) {
+  const int tile = blockIdx.x, h = blockIdx.y, sq = blockIdx.z;
+  const int ntile = gridDim.x;
+  u32x4* dst = kt_out + (((int64_t)sq * H + h) * ntile + tile) * 512;
+  const int64_t tok_stride = (int64_t)H * kHeadDim;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const f32x2 cs = table[t * 32 + 4 * u + e];
-    if (cs[1] != 0.0f) {
-      const float x = lo_bf16(w[e]), y = hi_bf16(w[e]);
-      r[e] = pack_bf16x2(__builtin_fmaf(x, cs[0], -y * cs[1]), __builtin_fmaf(x, cs[1], y * cs[0]));
-    } else {
-      r[e] = w[e];
+  for (int c = 0; c < 2; ++c) {
+    const int i = threadIdx.x + c * NT;
+    const int r = i >> 3, slot = i & 7;
+    const int key = tile * 64 + rho_key(r);
+    const int u = slot ^ (r & 7);
+    u32x4 w = {0u, 0u, 0u, 0u};
+    if (key < len) {
+      w = *(const u32x4*)(k + ((int64_t)sq * len + key) * tok_stride + h * kHeadDim + 8 * u);
+      if (table) {
+        const int t = (int)(((int64_t)sq * len + key) % rope_T);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const f32x2 cs = table[t * 32 + 4 * u + e];
+          if (cs[1] != 0.0f) {
+            const float x = lo_bf16(w[e]), y = hi_bf16(w[e]);
+            w[e] = pack_bf16x2(__builtin_fmaf(x, cs[0], -y * cs[1]), __builtin_fmaf(x, cs[1], y * cs[0]));
+          }
+        }
+      }
     }
+    dst[i] = w;
   }
-  dst[i] = r;
 }
 
-// grid (pad/64, H, nseq); tile = 64 keys x 64 channels through LDS
-__global__ __launch_bounds__(NT) void vt_kernel(const uint16_t* __restrict__ v, uint16_t* __restrict__ vt, int len,
-                                                int pad, int H, int64_t cols) {
-  __shared__ uint16_t tile[64][64 + 2];
-  const int j0 = blockIdx.x * 64, h = blockIdx.y, sq = blockIdx.z;
-  const int tid = threadIdx.x;
+// V [nseq*len][H][64] -> VT [nseq][H][ntile][64 channel rows][8 slots]: slot s of row d
+// holds keys 64*kt + 8u .. +7 of channel d, u = s ^ swz_vt(d); keys past len are zero.
+// grid (ntile, H, nseq); the 64 x 64 tile is transposed through LDS.
+__global__ __launch_bounds__(NT) void v_tiles_kernel(const uint16_t* __restrict__ v, u32x4* __restrict__ vt_out,
+                                                     int len, int H) {
+  __shared__ uint32_t tile_s[64][33];  // [key][channel pair], padded
+  const int tile = blockIdx.x, h = blockIdx.y, sq = blockIdx.z;
+  const int ntile = gridDim.x;
   const int64_t tok_stride = (int64_t)H * kHeadDim;
-  // load: 64 keys x 8 units of 16 bytes; thread -> (key = i / 8, unit = i % 8)
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
-    const int i = tid + c * NT;
-    const int j = i >> 3, u = i & 7;
+    const int i = threadIdx.x + c * NT;
+    const int j = i >> 3, u = i & 7;  // key, unit of 8 channels
+    const int key = tile * 64 + j;
     u32x4 w = {0u, 0u, 0u, 0u};
-    if (j0 + j < len) w = *(const u32x4*)(v + ((int64_t)sq * len + j0 + j) * tok_stride + h * kHeadDim + 8 * u);
+    if (key < len) w = *(const u32x4*)(v + ((int64_t)sq * len + key) * tok_stride + h * kHeadDim + 8 * u);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      tile[j][8 * u + 2 * e] = (uint16_t)(w[e] & 0xFFFFu);
-      tile[j][8 * u + 2 * e + 1] = (uint16_t)(w[e] >> 16);
-    }
+    for (int e = 0; e < 4; ++e) tile_s[j][4 * u + e] = w[e];
   }
   __syncthreads();
-  // store: 64 channel rows x 8 units of 8 keys
+  u32x4* dst = vt_out + (((int64_t)sq * H + h) * ntile + tile) * 512;
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
-    const int i = tid + c * NT;
-    const int d = i >> 3, u = i & 7;
+    const int i = threadIdx.x + c * NT;
+    const int d = i >> 3, slot = i & 7;
+    const int u = slot ^ swz_vt(d);
     u32x4 w;
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      w[e] = (uint32_t)tile[8 * u + 2 * e][d] | ((uint32_t)tile[8 * u + 2 * e + 1][d] << 16);
-    *(u32x4*)(vt + ((int64_t)h * kHeadDim + d) * cols + (int64_t)sq * pad + j0 + 8 * u) = w;
+    for (int e = 0; e < 4; ++e) {
+      const int j0 = 8 * u + 2 * e;  // keys j0, j0+1 of channel d
+      const uint32_t a = tile_s[j0][d >> 1], b = tile_s[j0 + 1][d >> 1];
+      w[e] = (d & 1) ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
+    }
+    dst[i] = w;
   }
 }
 
@@ -96,20 +111,20 @@ hipError_t launch_rope_table(const int32_t* pos_yx, int T, double base, void* ta
   return hipGetLastError();
 }
 
-hipError_t launch_rope_apply_bf16(const void* src, void* dst, int64_t n_tok, int H, int T, const void* table,
-                                  hipStream_t stream) {
-  const int64_t units = n_tok * H * 8;
-  if (units <= 0) return hipSuccess;
-  hipLaunchKernelGGL(rope_apply_kernel, dim3((unsigned)((units + NT - 1) / NT)), dim3(NT), 0, stream,
-                     (const u32x4*)src, (u32x4*)dst, units, H, T, (const f32x2*)table);
+hipError_t launch_k_tiles_bf16(const void* k, void* kt, int nseq, int len, int H, const void* table, int rope_T,
+                               hipStream_t stream) {
+  if (nseq <= 0 || len <= 0) return hipSuccess;
+  const int ntile = (len + 63) / 64;
+  hipLaunchKernelGGL(k_tiles_kernel, dim3((unsigned)ntile, (unsigned)H, (unsigned)nseq), dim3(NT), 0, stream,
+                     (const uint16_t*)k, (u32x4*)kt, len, H, (const f32x2*)table, rope_T);
   return hipGetLastError();
 }
 
-hipError_t launch_vt_bf16(const void* v, void* vt, int nseq, int len, int pad, int H, hipStream_t stream) {
+hipError_t launch_v_tiles_bf16(const void* v, void* vt, int nseq, int len, int H, hipStream_t stream) {
   if (nseq <= 0 || len <= 0) return hipSuccess;
-  const int64_t cols = (int64_t)nseq * pad;
-  hipLaunchKernelGGL(vt_kernel, dim3((unsigned)(pad / 64), (unsigned)H, (unsigned)nseq), dim3(NT), 0, stream,
-                     (const uint16_t*)v, (uint16_t*)vt, len, pad, H, cols);
+  const int ntile = (len + 63) / 64;
+  hipLaunchKernelGGL(v_tiles_kernel, dim3((unsigned)ntile, (unsigned)H, (unsigned)nseq), dim3(NT), 0, stream,
+                     (const uint16_t*)v, (u32x4*)vt, len, H);
   return hipGetLastError();
 }
 

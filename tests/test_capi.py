@@ -58,17 +58,17 @@ def test_workspace_queries(L):
     BF16, F32 = 0, 1
     S, T, H = 4, 261, 16
     tensor = S * T * H * 64
-    # bf16: V^T (keys padded to 64 per sequence); with RoPE also the table and rotated K
-    vt = H * 64 * S * 320 * 2
-    assert L.vggt_frame_attn_workspace(S, T, H, 0, BF16) == vt
-    assert L.vggt_frame_attn_workspace(S, T, H, 1, BF16) >= vt + tensor * 2 + T * 32 * 8
+    # bf16: K and V^T in 64-key tiles (keys padded to 64 per sequence); with RoPE also the cos/sin table
+    tiles = 2 * S * H * 5 * 64 * 64 * 2
+    assert L.vggt_frame_attn_workspace(S, T, H, 0, BF16) == tiles
+    assert L.vggt_frame_attn_workspace(S, T, H, 1, BF16) >= tiles + T * 32 * 8
     # fp32 debug: nothing without RoPE, rotated Q and K copies with it
     assert L.vggt_frame_attn_workspace(S, T, H, 0, F32) == 0
     assert L.vggt_frame_attn_workspace(S, T, H, 1, F32) >= 2 * tensor * 4
     # explicit splits add the fp32 partials (64 values + max + sum per row and head)
     n = S * T
     base = L.vggt_global_attn_workspace(S, T, H, 1, 0, BF16)
-    assert base >= H * 64 * 1088 * 2
+    assert base >= 2 * H * 17 * 64 * 64 * 2
     assert L.vggt_global_attn_workspace(S, T, H, 3, 0, BF16) >= base + 3 * n * H * (64 + 2) * 4
     assert L.vggt_global_attn_workspace(S, T, H, 1, 0, F32) == 0
     assert L.vggt_descriptor_xattn_workspace(100, 1374, 366, 16, 1, F32) == 0
