@@ -33,9 +33,33 @@ METRIC = "global-attention TFLOP/s + ms/layer at S frames; % of bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 
+# HBM traffic of one global-attention kernel launch on this workload, from
+# rocprofv3 FETCH_SIZE / WRITE_SIZE runs scaled by the counters' reading on a
+# plain 1 GiB copy (profiles/attn_fwd_bf16_vggt-518-s32_counters.md).  Valid
+# only for the kernel source it was measured on.
+PROFILED_TRAFFIC = {
+    "kernel_source_sha256": "9655204c72958de885d8684a77f30a2ae2089d162a58540c65e421097c295cc5",
+    "read_bytes": 1381.5e6,
+    "write_bytes": 416.5e6,
+}
+
 
 def attn_flops(nq: int, nk: int, H: int = 16, d: int = 64) -> float:
     return 4.0 * nq * nk * H * d
+
+
+def profiled_traffic():
+    """Bytes per launch if the attention kernel is the one the counters were taken on, else None."""
+    import hashlib
+
+    path = os.path.join(ROOT, "feed_forward_view_amd", "csrc", "attn_bf16.hip")
+    try:
+        sha = hashlib.sha256(open(path, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    if sha != PROFILED_TRAFFIC["kernel_source_sha256"]:
+        return None
+    return PROFILED_TRAFFIC["read_bytes"] + PROFILED_TRAFFIC["write_bytes"]
 
 
 def main() -> int:
@@ -105,11 +129,13 @@ def main() -> int:
         mark(4)
 
     if args.calibrate_copy_mib > 0:
-        n = args.calibrate_copy_mib << 20
-        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        # plain copy kernels of known size for hardware-counter calibration:
+        # an elementwise float32 copy (reads and writes N bytes each)
+        n = (args.calibrate_copy_mib << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
-        dst.copy_(src)
+        torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
         del src, dst
 
@@ -169,13 +195,13 @@ def main() -> int:
         "xattn_tflops": round(flops["xattn"] / (med["xattn"] * 1e-3) / 1e12, 2),
         "pool_gbs": round(pool_bytes / (med["pool"] * 1e-3) / 1e9, 1),
         "roofline": {
-            "kernel": "global attention call (attention kernel + RoPE pre-pass)",
+            "kernel": "global attention call (attn_fwd_bf16_kernel + K/V tile pre-passes + split merge)",
             "bound": "mfma",
             "achieved": round(g_tflops, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(g_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": profiled_traffic(),
         },
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "arch": getattr(props, "gcnArchName", "")},

@@ -32,7 +32,7 @@ constexpr int kMaxHeads = 128;
 constexpr int64_t kMaxTokens = int64_t(1) << 28;
 constexpr int kMaxSplits = 64;
 constexpr int kAssumedCUs = 256;       // MI355X; used only to size the key split
-constexpr int kWorkgroupsPerCU = 1;  // the bf16 kernel runs one 4-wave workgroup per CU
+constexpr int kWorkgroupsPerCU = 2;  // the bf16 kernel runs two 4-wave workgroups per CU
 
 // ---- device check, cached per device (read-only after first use)
 struct DevInfo {
