@@ -50,6 +50,8 @@
 // the 8 XCDs, so the linear id is remapped to give each XCD a contiguous run
 // of (query tile, head) work; the workgroups resident on one XCD then stream
 // the same head's keys and values through that XCD's L2.
+#include <type_traits>
+
 #include "common.h"
 
 namespace vggt {
@@ -206,10 +208,14 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
       for (int r = 0; r < 16; ++r) o[a][b][r] = 0.0f;
   float mref[2] = {0.0f, 0.0f};  // log2 units
   float lsum[2] = {0.0f, 0.0f};  // this lane's partial row sums
-  bool offs = false;             // some row of the wave has m != 0
+  f32x16 negm[2];                // -m of the lane's query, replicated: accumulator input of S^T
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) negm[qb][r] = 0.0f;
 
   f32x16 s0[2], s1[2];       // [kb] scores of query blocks 0 and 1
-  uint32_t p0[2][2][4], p1[2][2][4];
+  u32x4 p0[2][2], p1[2][2];  // [kb][j] bf16 pairs of keys 32kb+16j+8hi+0..7 (B operand of P V)
   bf16x8 kf[2][4];           // K fragments of the tile
   bf16x8 vf[2][2][2];        // V^T fragments [kb][j][db]
 
@@ -237,30 +243,30 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
         }
       }
   };
+  // S^T - m for one query block (the reference enters as the accumulator input)
   auto qk = [&](f32x16 (&s)[2], int qb) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const f32x16 z = {};
-      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb][0], qf[qb][0], z, 0, 0, 0);
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb][0], qf[qb][0], negm[qb], 0, 0, 0);
 #pragma unroll
       for (int dc = 1; dc < 4; ++dc)
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb][dc], qf[qb][dc], s[kb], 0, 0, 0);
     }
   };
-  auto pv = [&](const uint32_t (&pf)[2][2][4], int qb) {
+  auto pv = [&](const u32x4 (&pf)[2][2], int qb) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const u32x4 w = {pf[kb][j][0], pf[kb][j][1], pf[kb][j][2], pf[kb][j][3]};
 #pragma unroll
         for (int db = 0; db < 2; ++db)
-          o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kb][j][db], __builtin_bit_cast(bf16x8, w),
+          o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kb][j][db], __builtin_bit_cast(bf16x8, pf[kb][j]),
                                                               o[db][qb], 0, 0, 0);
       }
   };
-  // P = 2^(S - m) as bf16 pairs of keys 32kb+16j+8hi+0..7; returns the partial row sum
-  auto soft = [&](const f32x16 (&s)[2], bool sub, float m, uint32_t (&pf)[2][2][4]) -> float {
+  // P = 2^(S - m) as bf16 pairs of keys 32kb+16j+8hi+0..7 (S already has m subtracted, up to
+  // `shift`); returns the partial row sum
+  auto soft = [&](const f32x16 (&s)[2], bool sub, float shift, u32x4 (&pf)[2][2]) -> float {
     float acc = 0.0f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -270,8 +276,8 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
         for (int e = 0; e < 4; ++e) {
           float a = s[kb][8 * j + 2 * e], b = s[kb][8 * j + 2 * e + 1];
           if (sub) {
-            a -= m;
-            b -= m;
+            a -= shift;
+            b -= shift;
           }
           const uint32_t w = pack_bf16x2(__builtin_amdgcn_exp2f(a), __builtin_amdgcn_exp2f(b));
           pf[kb][j][e] = w;
@@ -279,32 +285,33 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
         }
     return acc;
   };
-  // slow path of one unit: move the reference if needed and redo its exponentials
-  auto slow = [&](const f32x16 (&s)[2], int qb, bool first, uint32_t (&pf)[2][2][4]) -> float {
+  // slow path of one query block: move the reference if needed and redo its exponentials
+  auto slow = [&](const f32x16 (&s)[2], int qb, bool first, u32x4 (&pf)[2][2]) -> float {
     float mx = s[0][0];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    float mnew = mref[qb];
+    // mx is relative to the current reference
+    float delta = 0.0f;
     if (first) {
-      if (mx < kLow || mx > kRaise) mnew = mx;
-    } else if (mx - mref[qb] > kRaise) {
-      mnew = mx;
+      if (mx < kLow || mx > kRaise) delta = mx;
+    } else if (mx > kRaise) {
+      delta = mx;
     }
-    if (__any(mnew != mref[qb])) {
-      const float alpha = __builtin_amdgcn_exp2f(mref[qb] - mnew);
+    if (__any(delta != 0.0f)) {
+      const float alpha = __builtin_amdgcn_exp2f(-delta);
       lsum[qb] *= alpha;
+      mref[qb] += delta;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         o[0][qb][r] *= alpha;
         o[1][qb][r] *= alpha;
+        negm[qb][r] = -mref[qb];
       }
-      mref[qb] = mnew;
-      offs = __any(mref[0] != 0.0f || mref[1] != 0.0f);
     }
-    return soft(s, true, mref[qb], pf);
+    return soft(s, true, delta, pf);
   };
   auto mask = [&](f32x16 (&s)[2], int kt) {
     // lane/reg -> key kt + 32*kb + 16*(r/8) + 8*hi + r%8
@@ -327,53 +334,53 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
     __syncthreads();
   };
 
-  // one tile: S^T of block 1 || exp of block 0, then P V of block 0 || exp of block 1
-  auto tile_body = [&](int t, bool masked) {
+  // One tile: S^T of block 1 || exp of block 0, then P V of block 0 || exp of block 1.
+  // FIRST: the reference is set by the slow path; LAST: keys past the end are masked.
+  auto tile_body = [&](int t, auto first_c, auto last_c) {
+    constexpr bool first = decltype(first_c)::value;
+    constexpr bool masked = decltype(last_c)::value;
     const int stage = t % NSTAGE;
-    const bool first = t == 0;
     read_k(stage);
     qk(s0, 0);
-    if (masked) mask(s0, kbeg + t * BK);
-    float ls0, ls1;
-    if (offs) {
-      qk(s1, 1);
-      ls0 = soft(s0, true, mref[0], p0);
-    } else {
-      qk(s1, 1);
-      ls0 = soft(s0, false, 0.0f, p0);
-      VGGT_INTERLEAVE(8, 8);
-    }
-    if (masked) mask(s1, kbeg + t * BK);
+    if constexpr (masked) mask(s0, kbeg + t * BK);
+    qk(s1, 1);
+    float ls0 = soft(s0, false, 0.0f, p0);
+    VGGT_INTERLEAVE(8, 8);
+    if constexpr (masked) mask(s1, kbeg + t * BK);
     if (first || __any(!(ls0 <= kSumLimit))) ls0 = slow(s0, 0, first, p0);
     lsum[0] += ls0;
     read_v(stage);
-    if (offs) {
-      pv(p0, 0);
-      ls1 = soft(s1, true, mref[1], p1);
-    } else {
-      pv(p0, 0);
-      ls1 = soft(s1, false, 0.0f, p1);
-      VGGT_INTERLEAVE(8, 8);
-    }
+    pv(p0, 0);
+    float ls1 = soft(s1, false, 0.0f, p1);
+    VGGT_INTERLEAVE(8, 8);
     if (first || __any(!(ls1 <= kSumLimit))) ls1 = slow(s1, 1, first, p1);
     lsum[1] += ls1;
     pv(p1, 1);
   };
+  using yes = std::true_type;
+  using no = std::false_type;
+  auto advance = [&](int t) {
+    land(t);
+    if (t + NSTAGE - 1 < ntiles) issue((t + NSTAGE - 1) % NSTAGE, t + NSTAGE - 1);
+  };
 
   if (active) {
-    for (int t = 0; t + 1 < ntiles; ++t) {
-      land(t);
-      if (t + NSTAGE - 1 < ntiles) issue((t + NSTAGE - 1) % NSTAGE, t + NSTAGE - 1);
-      tile_body(t, false);
+    if (ntiles == 1) {
+      advance(0);
+      tile_body(0, yes{}, yes{});
+    } else {
+      advance(0);
+      tile_body(0, yes{}, no{});
+      for (int t = 1; t + 1 < ntiles; ++t) {
+        advance(t);
+        tile_body(t, no{}, no{});
+      }
+      advance(ntiles - 1);
+      tile_body(ntiles - 1, no{}, yes{});
     }
-    land(ntiles - 1);
-    tile_body(ntiles - 1, kbeg + ntiles * BK > kend);
   } else {
     // keep the workgroup's barrier and load sequence
-    for (int t = 0; t < ntiles; ++t) {
-      land(t);
-      if (t + NSTAGE - 1 < ntiles) issue((t + NSTAGE - 1) % NSTAGE, t + NSTAGE - 1);
-    }
+    for (int t = 0; t < ntiles; ++t) advance(t);
     return;
   }
 
