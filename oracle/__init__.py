@@ -166,3 +166,31 @@ def descriptor_xattn(q, kd, vd, scale=None, rows=None, nthreads=None) -> np.ndar
     kf = to_f64(kd).reshape(-1, H, D)
     vf = to_f64(vd).reshape(-1, H, D)
     return attention(qf, kf, vf, scale=scale, rows=rows, nthreads=nthreads)
+
+
+def descriptor_stream_xattn(q, kd, vd, chunk_frames: int, scale=None, rows=None, nthreads=None) -> np.ndarray:
+    """Chunk-recursive descriptor attention (FlashVGGT project page, Overview:
+    online inference over long sequences that reuses the cached descriptors of
+    earlier chunks; Key Arguments: --chunksize, default 10 frames).
+
+    Frames are taken in consecutive chunks of `chunk_frames` (the last may be
+    shorter).  A query token of chunk c attends to the descriptors of every
+    frame of chunks 0..c, its own chunk included (the cache after chunk c has
+    been appended), in frame order.  q [S, T, H, D], kd/vd [S, Dn, H, D];
+    rows index the flattened [S*T] query axis.  float64 [len(rows) or S*T, H, D]."""
+    S, T, H, D = q.shape
+    Dn = kd.shape[1]
+    if chunk_frames < 1:
+        raise ValueError("chunk_frames must be >= 1")
+    qf = to_f64(q).reshape(S * T, H, D)
+    kf = to_f64(kd).reshape(S * Dn, H, D)
+    vf = to_f64(vd).reshape(S * Dn, H, D)
+    want = np.arange(S * T, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64).reshape(-1)
+    out = np.zeros((want.size, H, D), dtype=np.float64)
+    for c in range((S + chunk_frames - 1) // chunk_frames):
+        f_end = min(S, (c + 1) * chunk_frames)  # frames whose descriptors are cached after chunk c
+        sel = (want >= c * chunk_frames * T) & (want < f_end * T)
+        if sel.any():
+            out[sel] = attention(qf, kf[:f_end * Dn], vf[:f_end * Dn], scale=scale, rows=want[sel],
+                                 nthreads=nthreads)
+    return out

@@ -264,8 +264,9 @@ def test_xattn_small_full_and_unit_window():
     kp, vp = ffv.vggt_descriptor_pool(kd, vd, 12, 12, 5, 2, 2)
     kpr = oracle.descriptor_pool(k, wl.S, wl.T, 12, 12, 5, 2, 2)
     vpr = oracle.descriptor_pool(v, wl.S, wl.T, 12, 12, 5, 2, 2)
-    # the oracle sees the GPU's own bf16 descriptors, so only the attention is compared
-    ref = oracle.descriptor_xattn(q, to_f64(kp), to_f64(vp))
+    # descriptors as the pool stores them: the oracle's means rounded to bf16 (RNE) on the host
+    ref = oracle.descriptor_xattn(q, workload.f32_to_bf16_bits(kpr.astype(np.float32)),
+                                  workload.f32_to_bf16_bits(vpr.astype(np.float32)))
     for splits in (0, 1, 3):
         check_bf16(to_f64(ffv.vggt_descriptor_xattn(qd, kp, vp, kv_splits=splits)), ref, f"xattn splits={splits}")
     # and end to end against the oracle's own pooled descriptors

@@ -360,6 +360,74 @@ def test_xattn_with_unit_window_equals_global_attention():
                                rtol=1e-12, atol=1e-14)
 
 
+def _masked_einsum_attention(q, k, v, allowed, scale):
+    # brute force with an explicit [query, key] visibility matrix
+    s = np.einsum("qhd,khd->hqk", q, k) * scale
+    s = np.where(allowed[None], s, -np.inf)
+    p = np.exp(s - s.max(axis=-1, keepdims=True))
+    p /= p.sum(axis=-1, keepdims=True)
+    return np.einsum("hqk,khd->qhd", p, v)
+
+
+@pytest.mark.parametrize("S,F", [(5, 2), (4, 1), (3, 3), (3, 7)])
+def test_stream_xattn_brute_force(S, F):
+    wl = workload.Workload("t", 8, S=S, gh=3, gw=3, n_special=2, patch_begin=1, H=2, D=64)
+    q, k, v = wl.qkv_bf16()
+    T = wl.T
+    kd = oracle.descriptor_pool(k, S, T, 3, 3, 1, 2, 2)
+    vd = oracle.descriptor_pool(v, S, T, 3, 3, 1, 2, 2)
+    Dn = kd.shape[1]
+    q_frame = np.repeat(np.arange(S), T)
+    k_frame = np.repeat(np.arange(S), Dn)
+    # a query of frame f sees the descriptors of frames before the end of f's chunk
+    allowed = k_frame[None, :] < ((q_frame // F + 1) * F)[:, None]
+    ref = _masked_einsum_attention(oracle.to_f64(q).reshape(S * T, 2, 64), kd.reshape(-1, 2, 64),
+                                   vd.reshape(-1, 2, 64), allowed, 0.125)
+    got = oracle.descriptor_stream_xattn(q, kd, vd, F)
+    np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-13)
+    rows = np.array([0, T - 1, T, S * T - 1])
+    np.testing.assert_array_equal(oracle.descriptor_stream_xattn(q, kd, vd, F, rows=rows), got[rows])
+    if F >= S:
+        # one chunk holds every frame: the single-forward descriptor attention
+        np.testing.assert_array_equal(got, oracle.descriptor_xattn(q, kd, vd))
+
+
+def test_stream_xattn_is_causal_over_chunks_and_averages_prefix():
+    S, F = 5, 2
+    wl = workload.Workload("t", 9, S=S, gh=4, gw=4, n_special=1, patch_begin=0, H=1, D=64)
+    q, k, v = wl.qkv_bf16()
+    T = wl.T
+    kd = oracle.descriptor_pool(k, S, T, 4, 4, 0, 2, 2)
+    vd = oracle.descriptor_pool(v, S, T, 4, 4, 0, 2, 2)
+    Dn = kd.shape[1]
+    base = oracle.descriptor_stream_xattn(q, kd, vd, F)
+    # changing the frames of the last chunk leaves every earlier chunk unchanged
+    kd2, vd2 = kd.copy(), vd.copy()
+    kd2[4] += 3.0
+    vd2[4] -= 1.0
+    alt = oracle.descriptor_stream_xattn(q, kd2, vd2, F)
+    np.testing.assert_array_equal(alt[:4 * T], base[:4 * T])
+    assert np.abs(alt[4 * T:] - base[4 * T:]).max() > 1e-3
+    # identical (zero) keys: each chunk's output is the mean of the cached value rows
+    zero = np.zeros_like(kd)
+    got = oracle.descriptor_stream_xattn(q, zero, vd, F)
+    for c, f_end in enumerate((2, 4, 5)):
+        mean = vd[:f_end].reshape(f_end * Dn, 1, 64).mean(axis=0)
+        rows = slice(c * F * T, min(S, (c + 1) * F) * T)
+        np.testing.assert_allclose(got[rows], np.broadcast_to(mean, got[rows].shape), rtol=1e-13, atol=1e-15)
+
+
+def test_stream_xattn_first_chunk_of_one_frame_is_frame_attention():
+    # unit pooling window and one frame per chunk: chunk 0 attends to frame 0's own tokens
+    wl = workload.Workload("t", 10, S=3, gh=3, gw=4, n_special=2, patch_begin=2, H=2, D=64)
+    q, k, v = wl.qkv_bf16()
+    T = wl.T
+    kd = oracle.descriptor_pool(k, wl.S, T, 3, 4, 2, 1, 1)
+    vd = oracle.descriptor_pool(v, wl.S, T, 3, 4, 2, 1, 1)
+    got = oracle.descriptor_stream_xattn(q, kd, vd, 1)
+    np.testing.assert_allclose(got[:T], oracle.frame_attn(q, k, v, wl.S, T)[:T], rtol=1e-12, atol=1e-14)
+
+
 # --------------------------------------------------------------------------
 # Input generator
 # --------------------------------------------------------------------------
