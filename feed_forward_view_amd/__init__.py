@@ -40,6 +40,11 @@ SIGNATURES = {
     "vggt_descriptor_pool": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i, _vp]),
     "vggt_descriptor_xattn_workspace": (_sz, [_i, _i, _i, _i, _i, _i]),
     "vggt_descriptor_xattn": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]),
+    "vggt_descriptor_cache_bytes": (_sz, [_i, _i, _i]),
+    "vggt_descriptor_cache_append": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _i, _vp]),
+    "vggt_descriptor_cache_attn_workspace": (_sz, [_i, _i, _i, _i, _i]),
+    "vggt_descriptor_cache_attn": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]),
+    "vggt_descriptor_chunked_xattn": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp]),
 }
 
 _lib = None
@@ -214,3 +219,97 @@ def vggt_descriptor_xattn(q, kd, vd, out=None, scale=0.0, kv_splits=0, workspace
            lib().vggt_descriptor_xattn(_ptr(q), _ptr(kd), _ptr(vd), _ptr(out), _dtype_code(q), S, T, Dn, H, scale,
                                        kv_splits, _ptr(ws), nbytes, _stream(stream)))
     return out
+
+
+# ---------------------------------------------------------------------------
+# FlashVGGT chunk-recursive attention over a descriptor cache
+# ---------------------------------------------------------------------------
+
+def _code(dtype) -> int:
+    if dtype == torch.bfloat16:
+        return BF16
+    if dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {dtype}; use bfloat16 or float32")
+
+
+def vggt_descriptor_cache_bytes(capacity: int, H: int, dtype=torch.bfloat16) -> int:
+    return int(lib().vggt_descriptor_cache_bytes(capacity, H, _code(dtype)))
+
+
+def vggt_descriptor_cache_append(cache: torch.Tensor, capacity: int, H: int, used: int, kd: torch.Tensor,
+                                 vd: torch.Tensor, dtype=None, stream=None) -> int:
+    """Append descriptors kd/vd [..., H, 64] (flattened to [n, H, 64]) at position `used` of the
+    cache buffer (uint8 device tensor); returns the new count."""
+    dtype = kd.dtype if dtype is None else dtype
+    for n, t in (("kd", kd), ("vd", vd)):
+        if t.dtype != dtype or t.shape[-2:] != (H, HEAD_DIM) or not t.is_contiguous() or t.device.type != "cuda":
+            raise ValueError(f"{n} must be a contiguous GPU tensor [..., {H}, 64] of {dtype}")
+    n = kd.numel() // (H * HEAD_DIM)
+    if vd.numel() != kd.numel():
+        raise ValueError("kd and vd must hold the same number of descriptors")
+    _check("vggt_descriptor_cache_append",
+           lib().vggt_descriptor_cache_append(_ptr(cache), _code(dtype), capacity, H, used, _ptr(kd), _ptr(vd), n,
+                                              _stream(stream)))
+    return used + n
+
+
+def vggt_descriptor_cache_attn_workspace(nq: int, used: int, H: int, kv_splits: int, dtype=torch.bfloat16) -> int:
+    return int(lib().vggt_descriptor_cache_attn_workspace(nq, used, H, kv_splits, _code(dtype)))
+
+
+def vggt_descriptor_cache_attn(q: torch.Tensor, cache: torch.Tensor, capacity: int, used: int, out=None, scale=0.0,
+                               kv_splits=0, workspace=None, stream=None) -> torch.Tensor:
+    """Query tokens q [..., H, 64] attend to the first `used` cached descriptors; returns out (q's shape)."""
+    H = int(q.shape[-2])
+    if q.shape[-1] != HEAD_DIM or not q.is_contiguous() or q.device.type != "cuda":
+        raise ValueError("q must be a contiguous GPU tensor [..., H, 64]")
+    nq = q.numel() // (H * HEAD_DIM)
+    out = torch.empty_like(q) if out is None else out
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must match q")
+    need = vggt_descriptor_cache_attn_workspace(nq, used, H, kv_splits, q.dtype)
+    ws, nbytes = _workspace(need, q.device, workspace)
+    _check("vggt_descriptor_cache_attn",
+           lib().vggt_descriptor_cache_attn(_ptr(q), _ptr(cache), _ptr(out), _dtype_code(q), capacity, H, used, nq,
+                                            scale, kv_splits, _ptr(ws), nbytes, _stream(stream)))
+    return out
+
+
+def vggt_descriptor_chunked_xattn(q: torch.Tensor, cache: torch.Tensor, capacity: int, Dn: int, chunk_frames: int,
+                                  out=None, scale=0.0, stream=None) -> torch.Tensor:
+    """All chunks in one launch: q [S, T, H, 64]; the cache holds the S*Dn descriptors of all frames."""
+    S, T, H = _tok(q, "q")
+    out = torch.empty_like(q) if out is None else out
+    if _tok(out, "out") != (S, T, H) or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    _check("vggt_descriptor_chunked_xattn",
+           lib().vggt_descriptor_chunked_xattn(_ptr(q), _ptr(cache), _ptr(out), _dtype_code(q), capacity, H, S, T, Dn,
+                                               chunk_frames, scale, _stream(stream)))
+    return out
+
+
+class DescriptorCache:
+    """Caller-side bookkeeping for one descriptor cache: the device buffer, its
+    capacity and the number of descriptors appended so far."""
+
+    def __init__(self, capacity: int, H: int = 16, dtype=torch.bfloat16, device="cuda"):
+        nbytes = vggt_descriptor_cache_bytes(capacity, H, dtype)
+        if nbytes == 0:
+            raise ValueError("bad cache shape")
+        self.capacity, self.H, self.dtype = capacity, H, dtype
+        self.buffer = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.used = 0
+
+    def append(self, kd: torch.Tensor, vd: torch.Tensor, stream=None) -> int:
+        self.used = vggt_descriptor_cache_append(self.buffer, self.capacity, self.H, self.used, kd, vd, self.dtype,
+                                                 stream)
+        return self.used
+
+    def attend(self, q: torch.Tensor, out=None, scale=0.0, kv_splits=0, workspace=None, stream=None) -> torch.Tensor:
+        return vggt_descriptor_cache_attn(q, self.buffer, self.capacity, self.used, out, scale, kv_splits, workspace,
+                                          stream)
+
+    def attend_chunked(self, q: torch.Tensor, Dn: int, chunk_frames: int, out=None, scale=0.0,
+                       stream=None) -> torch.Tensor:
+        return vggt_descriptor_chunked_xattn(q, self.buffer, self.capacity, Dn, chunk_frames, out, scale, stream)

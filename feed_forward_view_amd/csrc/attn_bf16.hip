@@ -127,19 +127,23 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
   const int head = rest % p.H;
   rest /= p.H;
   const int split = rest % p.splits;
-  const int seq = rest / p.splits;
+  // with growing key prefixes the longest sequences are started first
+  const int seq = p.nk_step > 0 ? p.nseq - 1 - rest / p.splits : rest / p.splits;
+  const int nq_seq = (int)min((int64_t)p.nq, p.nq_total - (int64_t)seq * p.nq);
+  const int nk_seq = p.nk_step > 0 ? (int)min((int64_t)p.nk, (int64_t)(seq + 1) * p.nk_step) : p.nk;
 
   const uint16_t* __restrict__ qg = (const uint16_t*)p.q + (seq * p.q_seq_stride) * p.tok_stride + head * D;
   // K and V^T tiles of this (sequence, head): 512 16-byte units per tile
-  const u32x4* __restrict__ ktg = (const u32x4*)p.k + ((int64_t)seq * p.H + head) * p.ktiles_seq * 512;
-  const u32x4* __restrict__ vtg = (const u32x4*)p.vt + ((int64_t)seq * p.H + head) * p.ktiles_seq * 512;
+  const int64_t kseq = p.k_seq_stride != 0 ? seq : 0;
+  const u32x4* __restrict__ ktg = (const u32x4*)p.k + (kseq * p.H + head) * p.ktiles_seq * 512;
+  const u32x4* __restrict__ vtg = (const u32x4*)p.vt + (kseq * p.H + head) * p.ktiles_seq * 512;
 
   const int kbeg = split * p.keys_per_split;
-  const int kend = min(p.nk, kbeg + p.keys_per_split);
+  const int kend = min(nk_seq, kbeg + p.keys_per_split);
   const int ntiles = (kend - kbeg + BK - 1) / BK;
 
   const int q0 = qt * BQ + wave * 64;  // first query of this wave
-  const bool active = q0 < p.nq;
+  const bool active = q0 < nq_seq;
 
   // ---- tile loads: each wave copies two 1 KiB blocks of the K tile and two of the V^T tile
   const int ktile0 = kbeg / BK;
@@ -165,7 +169,7 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const int qi = q0 + 32 * qb + l32;
-      const bool ok = qi < p.nq;
+      const bool ok = qi < nq_seq;
       const int qrow = ok ? qi : 0;
       const int tpos = tab ? (int)((seq * p.q_seq_stride + qrow) % p.rope_T) : 0;
       const f32x2* trow = tab ? tab + tpos * 32 + 4 * hi : nullptr;
@@ -389,7 +393,7 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
   for (int qb = 0; qb < 2; ++qb) {
     const float ltot = lsum[qb] + __shfl_xor(lsum[qb], 32);
     const int qi = q0 + 32 * qb + l32;
-    if (qi >= p.nq) continue;
+    if (qi >= nq_seq) continue;
     if (p.splits == 1) {
       const float inv = 1.0f / ltot;
       uint16_t* og = (uint16_t*)p.o + (seq * p.q_seq_stride + qi) * p.tok_stride + head * D;

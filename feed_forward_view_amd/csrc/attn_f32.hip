@@ -29,16 +29,18 @@ __global__ __launch_bounds__(NT) void attn_fwd_f32_kernel(AttnProblem p) {
   const int head = rest % p.H;
   rest /= p.H;
   const int split = rest % p.splits;
-  const int seq = rest / p.splits;
+  const int seq = p.nk_step > 0 ? p.nseq - 1 - rest / p.splits : rest / p.splits;
+  const int nq_seq = (int)min((int64_t)p.nq, p.nq_total - (int64_t)seq * p.nq);
+  const int nk_seq = p.nk_step > 0 ? (int)min((int64_t)p.nk, (int64_t)(seq + 1) * p.nk_step) : p.nk;
 
   const float* __restrict__ qg = (const float*)p.q + (seq * p.q_seq_stride) * p.tok_stride + head * D;
   const float* __restrict__ kg = (const float*)p.k + (seq * p.k_seq_stride) * p.tok_stride + head * D;
   const float* __restrict__ vg = (const float*)p.v + (seq * p.k_seq_stride) * p.tok_stride + head * D;
 
   const int kbeg = split * p.keys_per_split;
-  const int kend = min(p.nk, kbeg + p.keys_per_split);
+  const int kend = min(nk_seq, kbeg + p.keys_per_split);
   const int qi = qt * BQ + tid;
-  const bool valid = qi < p.nq;
+  const bool valid = qi < nq_seq;
 
   float q[D], acc[D];
 #pragma unroll

@@ -427,3 +427,159 @@ VGGT_API vggt_status vggt_descriptor_xattn(const void* q, const void* kd, const 
   if (e != hipSuccess) return device_error("descriptor attention launch", e);
   return VGGT_OK;
 }
+
+// ---------------------------------------------------------------------------
+// FlashVGGT chunk-recursive attention over a descriptor cache
+// ---------------------------------------------------------------------------
+
+namespace {
+
+// Where K and V live inside a cache buffer.
+struct CacheView {
+  int cap_tiles = 0;  // bf16: 64-descriptor tiles per head
+  size_t k_bytes = 0;
+  size_t total = 0;
+};
+
+bool cache_dims_ok(int capacity, int H) { return capacity >= 1 && capacity < kMaxTokens && H >= 1 && H <= kMaxHeads; }
+
+CacheView cache_view(int capacity, int H, vggt_dtype dt) {
+  CacheView c;
+  if (dt == VGGT_BF16) {
+    c.cap_tiles = (capacity + 63) / 64;
+    c.k_bytes = (size_t)H * c.cap_tiles * 64 * vggt::kHeadDim * 2;
+  } else {
+    c.k_bytes = (size_t)capacity * H * vggt::kHeadDim * 4;
+  }
+  c.total = 2 * c.k_bytes;
+  return c;
+}
+
+vggt::AttnProblem cache_problem(const void* q, const void* cache, const CacheView& c, void* o, int H, float scale,
+                                vggt_dtype dt) {
+  const char* base = (const char*)cache;
+  vggt::AttnProblem p = base_problem(q, base, nullptr, o, H, scale);
+  if (dt == VGGT_BF16) {
+    p.vt = base + c.k_bytes;
+    p.ktiles_seq = c.cap_tiles;
+  } else {
+    p.v = base + c.k_bytes;
+  }
+  p.k_seq_stride = 0;  // every query sequence reads the one cache
+  return p;
+}
+
+Layout partials_layout(int64_t nq, int64_t nk, int H, int kv_splits, vggt_dtype dt) {
+  Layout L;
+  L.sp = plan_splits(nq, nk, H, kv_splits, dt);
+  if (L.sp.splits > 1) {
+    add(L, L.part_o, (size_t)L.sp.splits * nq * H * vggt::kHeadDim * 4);
+    add(L, L.part_ml, (size_t)L.sp.splits * nq * H * 2 * 4);
+  }
+  return L;
+}
+
+}  // namespace
+
+VGGT_API size_t vggt_descriptor_cache_bytes(int capacity, int H, vggt_dtype dt) {
+  if (!dtype_ok(dt) || !cache_dims_ok(capacity, H)) return 0;
+  return cache_view(capacity, H, dt).total;
+}
+
+VGGT_API vggt_status vggt_descriptor_cache_append(void* cache, vggt_dtype dt, int capacity, int H, int used,
+                                                  const void* kd, const void* vd, int n, void* stream) {
+  g_last_error[0] = 0;
+  if (!dtype_ok(dt)) return fail(VGGT_ERR_UNSUPPORTED, "unknown dtype %d", (int)dt);
+  if (!cache_dims_ok(capacity, H)) return fail(VGGT_ERR_SHAPE, "bad cache shape capacity=%d H=%d", capacity, H);
+  if (used < 0 || n < 0 || (int64_t)used + n > capacity)
+    return fail(VGGT_ERR_SHAPE, "append of %d descriptors at %d exceeds capacity %d", n, used, capacity);
+  if (n == 0) return VGGT_OK;
+  if (!cache || !kd || !vd) return fail(VGGT_ERR_NULL, "cache, kd and vd are required");
+  if (!aligned16(cache) || !aligned16(kd) || !aligned16(vd)) return fail(VGGT_ERR_ALIGN, "misaligned pointer");
+  const CacheView c = cache_view(capacity, H, dt);
+  const size_t in_b = (size_t)n * H * vggt::kHeadDim * elem_size(dt);
+  if (overlap(cache, c.total, kd, in_b) || overlap(cache, c.total, vd, in_b))
+    return fail(VGGT_ERR_ALIAS, "kd/vd overlap the cache");
+  if (vggt_status s = check_device()) return s;
+  char* base = (char*)cache;
+  const hipStream_t st = (hipStream_t)stream;
+  hipError_t e;
+  if (dt == VGGT_BF16) {
+    e = vggt::launch_tiles_append_bf16(kd, vd, base, base + c.k_bytes, c.cap_tiles, used, n, H, st);
+  } else {
+    const size_t off = (size_t)used * H * vggt::kHeadDim * 4;
+    e = hipMemcpyAsync(base + off, kd, in_b, hipMemcpyDeviceToDevice, st);
+    if (e == hipSuccess) e = hipMemcpyAsync(base + c.k_bytes + off, vd, in_b, hipMemcpyDeviceToDevice, st);
+  }
+  if (e != hipSuccess) return device_error("descriptor cache append", e);
+  return VGGT_OK;
+}
+
+VGGT_API size_t vggt_descriptor_cache_attn_workspace(int nq, int used, int H, int kv_splits, vggt_dtype dt) {
+  if (!dtype_ok(dt) || nq < 0 || nq >= kMaxTokens || !cache_dims_ok(used, H) || kv_splits < 0 ||
+      kv_splits > kMaxSplits)
+    return 0;
+  if (nq == 0) return 0;
+  return partials_layout(nq, used, H, kv_splits, dt).total;
+}
+
+VGGT_API vggt_status vggt_descriptor_cache_attn(const void* q, const void* cache, void* o, vggt_dtype dt, int capacity,
+                                                int H, int used, int nq, float scale, int kv_splits, void* workspace,
+                                                size_t ws_bytes, void* stream) {
+  g_last_error[0] = 0;
+  if (!dtype_ok(dt)) return fail(VGGT_ERR_UNSUPPORTED, "unknown dtype %d", (int)dt);
+  if (!cache_dims_ok(capacity, H) || used < 1 || used > capacity || nq < 0 || nq >= kMaxTokens)
+    return fail(VGGT_ERR_SHAPE, "bad shape capacity=%d H=%d used=%d nq=%d", capacity, H, used, nq);
+  if (kv_splits < 0 || kv_splits > kMaxSplits) return fail(VGGT_ERR_SHAPE, "kv_splits must be in [0, %d]", kMaxSplits);
+  if (nq == 0) return VGGT_OK;
+  const CacheView c = cache_view(capacity, H, dt);
+  const size_t q_b = (size_t)nq * H * vggt::kHeadDim * elem_size(dt);
+  const Layout L = partials_layout(nq, used, H, kv_splits, dt);
+  // the cache plays the role of both k and v in the overlap checks
+  if (vggt_status s = validate_attn({q, cache, cache, o}, nullptr, 0.0f, L.total, workspace, ws_bytes, q_b, c.total))
+    return s;
+  if (vggt_status s = check_device()) return s;
+  vggt::AttnProblem p = cache_problem(q, cache, c, o, H, scale, dt);
+  p.nq = nq;
+  p.nk = used;
+  p.nseq = 1;
+  p.nq_total = nq;
+  p.splits = L.sp.splits;
+  p.keys_per_split = L.sp.keys_per_split;
+  if (L.sp.splits > 1) {
+    p.part_o = (float*)((char*)workspace + L.part_o);
+    p.part_ml = (float*)((char*)workspace + L.part_ml);
+  }
+  hipError_t e = run_attention(p, dt, (hipStream_t)stream);
+  if (e != hipSuccess) return device_error("descriptor cache attention launch", e);
+  return VGGT_OK;
+}
+
+VGGT_API vggt_status vggt_descriptor_chunked_xattn(const void* q, const void* cache, void* o, vggt_dtype dt,
+                                                   int capacity, int H, int S, int T, int Dn, int chunk_frames,
+                                                   float scale, void* stream) {
+  g_last_error[0] = 0;
+  if (!dtype_ok(dt)) return fail(VGGT_ERR_UNSUPPORTED, "unknown dtype %d", (int)dt);
+  if (!cache_dims_ok(capacity, H) || !tokens_ok(S, T, H) || Dn < 1 || chunk_frames < 1 ||
+      (int64_t)S * Dn > capacity)
+    return fail(VGGT_ERR_SHAPE, "bad shape capacity=%d H=%d S=%d T=%d Dn=%d chunk_frames=%d", capacity, H, S, T, Dn,
+                chunk_frames);
+  if (S == 0) return VGGT_OK;
+  const CacheView c = cache_view(capacity, H, dt);
+  const size_t q_b = (size_t)S * T * H * vggt::kHeadDim * elem_size(dt);
+  if (vggt_status s = validate_attn({q, cache, cache, o}, nullptr, 0.0f, 0, nullptr, 0, q_b, c.total)) return s;
+  if (vggt_status s = check_device()) return s;
+  const int F = std::min(chunk_frames, S);
+  vggt::AttnProblem p = cache_problem(q, cache, c, o, H, scale, dt);
+  p.nseq = (S + F - 1) / F;
+  p.nq = F * T;
+  p.q_seq_stride = (int64_t)F * T;
+  p.nq_total = (int64_t)S * T;
+  p.nk = S * Dn;
+  p.nk_step = F * Dn;
+  p.splits = 1;
+  p.keys_per_split = (int)pad64(p.nk);
+  hipError_t e = run_attention(p, dt, (hipStream_t)stream);
+  if (e != hipSuccess) return device_error("chunked descriptor attention launch", e);
+  return VGGT_OK;
+}

@@ -46,10 +46,13 @@ struct AttnProblem {
   float* part_ml;          // [splits][nq_total][H][2]: (max in log2 units, sum)
   int64_t tok_stride;      // elements between consecutive tokens (= H*64)
   int64_t q_seq_stride;    // tokens between sequence starts of q / o
-  int64_t k_seq_stride;    // tokens between sequence starts of k / v
-  int64_t nq_total;        // query tokens over all sequences (partial rows)
+  int64_t k_seq_stride;    // tokens between sequence starts of k / v (0: all sequences
+                           // share one key set, and in the bf16 kernel one set of tiles)
+  int64_t nq_total;        // query tokens over all sequences; the last sequence may hold
+                           // fewer than nq
   int nq;                  // queries per sequence
   int nk;                  // keys per sequence
+  int nk_step;             // > 0: sequence s sees only its first min(nk, (s+1)*nk_step) keys
   int nseq;                // sequences
   int H;                   // heads
   int splits;              // key ranges per sequence
@@ -68,6 +71,11 @@ hipError_t launch_rope_table(const int32_t* pos_yx, int T, double base, void* ta
 hipError_t launch_k_tiles_bf16(const void* k, void* kt, int nseq, int len, int H, const void* table, int rope_T,
                                hipStream_t stream);
 hipError_t launch_v_tiles_bf16(const void* v, void* vt, int nseq, int len, int H, hipStream_t stream);
+// Append n keys (K and V [n][H][64] bf16) to single-sequence tile buffers that own
+// dst_ntile tiles per head, at key offset key0; keys of the last tile past key0 + n are
+// zeroed, keys below key0 are kept.
+hipError_t launch_tiles_append_bf16(const void* k, const void* v, void* kt, void* vt, int dst_ntile, int key0, int n,
+                                    int H, hipStream_t stream);
 hipError_t launch_pool(const void* k, const void* v, void* kd, void* vd, bool bf16, int S, int T, int H, int gh,
                        int gw, int patch_begin, int ph, int pw, int Dn, hipStream_t stream);
 

@@ -32,20 +32,24 @@ __device__ __forceinline__ int rho_key(int i) { return (i & ~0xC) | ((i & 4) << 
 __device__ __forceinline__ int swz_vt(int d) { return (d ^ (d >> 3)) & 7; }
 
 // K [nseq*len][H][64] -> KT [nseq][H][ntile][64 rows][8 slots of 16 bytes]: row r of tile
-// kt holds key 64*kt + rho(r), slot s holds its channels 8u..8u+7 with u = s ^ (r & 7); keys
-// past len are zero.  With a table, pairs are rotated as in rope_apply_kernel (the
-// position of key j of sequence q is (q*len + j) % rope_T).  grid (ntile, H, nseq).
+// kt holds key 64*kt + rho(r), slot s holds its channels 8u..8u+7 with u = s ^ (r & 7).
+// Source key j lands on tile key key0 + j; tile keys below key0 keep what the buffer
+// holds (appending to a filled prefix), tile keys at or past key0 + len become zero.
+// With a table, pairs are rotated as in rope_apply_kernel (the position of source key j
+// of sequence q is (q*len + j) % rope_T).  grid (tiles written, H, nseq); the first
+// tile written is key0 / 64 and each (sequence, head) owns dst_ntile tiles.
 __global__ __launch_bounds__(NT) void k_tiles_kernel(const uint16_t* __restrict__ k, u32x4* __restrict__ kt_out,
-                                                     int len, int H, const f32x2* __restrict__ table, int rope_T) {
-  const int tile = blockIdx.x, h = blockIdx.y, sq = blockIdx.z;
-  const int ntile = gridDim.x;
-  u32x4* dst = kt_out + (((int64_t)sq * H + h) * ntile + tile) * 512;
+                                                     int len, int H, const f32x2* __restrict__ table, int rope_T,
+                                                     int key0, int dst_ntile) {
+  const int tile = key0 / 64 + blockIdx.x, h = blockIdx.y, sq = blockIdx.z;
+  u32x4* dst = kt_out + (((int64_t)sq * H + h) * dst_ntile + tile) * 512;
   const int64_t tok_stride = (int64_t)H * kHeadDim;
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     const int i = threadIdx.x + c * NT;
     const int r = i >> 3, slot = i & 7;
-    const int key = tile * 64 + rho_key(r);
+    const int key = tile * 64 + rho_key(r) - key0;  // source key
+    if (key < 0) continue;
     const int u = slot ^ (r & 7);
     u32x4 w = {0u, 0u, 0u, 0u};
     if (key < len) {
@@ -67,37 +71,50 @@ __global__ __launch_bounds__(NT) void k_tiles_kernel(const uint16_t* __restrict_
 }
 
 // V [nseq*len][H][64] -> VT [nseq][H][ntile][64 channel rows][8 slots]: slot s of row d
-// holds keys 64*kt + 8u .. +7 of channel d, u = s ^ swz_vt(d); keys past len are zero.
-// grid (ntile, H, nseq); the 64 x 64 tile is transposed through LDS.
+// holds tile keys 8u .. 8u+7 of channel d, u = s ^ swz_vt(d).  Source key j lands on tile
+// key key0 + j; tile keys below key0 keep their contents (a slot that straddles key0 is
+// merged with what the buffer holds), tile keys at or past key0 + len become zero.
+// grid (tiles written, H, nseq) as for k_tiles_kernel; the 64 x 64 tile is transposed
+// through LDS.
 __global__ __launch_bounds__(NT) void v_tiles_kernel(const uint16_t* __restrict__ v, u32x4* __restrict__ vt_out,
-                                                     int len, int H) {
+                                                     int len, int H, int key0, int dst_ntile) {
   __shared__ uint32_t tile_s[64][33];  // [key][channel pair], padded
-  const int tile = blockIdx.x, h = blockIdx.y, sq = blockIdx.z;
-  const int ntile = gridDim.x;
+  const int tile = key0 / 64 + blockIdx.x, h = blockIdx.y, sq = blockIdx.z;
   const int64_t tok_stride = (int64_t)H * kHeadDim;
+  const int kfirst = tile * 64 - key0;  // source key of tile key 0
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     const int i = threadIdx.x + c * NT;
-    const int j = i >> 3, u = i & 7;  // key, unit of 8 channels
-    const int key = tile * 64 + j;
+    const int j = i >> 3, u = i & 7;  // tile key, unit of 8 channels
+    const int key = kfirst + j;
     u32x4 w = {0u, 0u, 0u, 0u};
-    if (key < len) w = *(const u32x4*)(v + ((int64_t)sq * len + key) * tok_stride + h * kHeadDim + 8 * u);
+    if (key >= 0 && key < len) w = *(const u32x4*)(v + ((int64_t)sq * len + key) * tok_stride + h * kHeadDim + 8 * u);
 #pragma unroll
     for (int e = 0; e < 4; ++e) tile_s[j][4 * u + e] = w[e];
   }
   __syncthreads();
-  u32x4* dst = vt_out + (((int64_t)sq * H + h) * ntile + tile) * 512;
+  u32x4* dst = vt_out + (((int64_t)sq * H + h) * dst_ntile + tile) * 512;
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     const int i = threadIdx.x + c * NT;
     const int d = i >> 3, slot = i & 7;
     const int u = slot ^ swz_vt(d);
+    const int kept = -kfirst - 8 * u;  // leading keys of this slot that stay as they are
+    if (kept >= 8) continue;
     u32x4 w;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int j0 = 8 * u + 2 * e;  // keys j0, j0+1 of channel d
       const uint32_t a = tile_s[j0][d >> 1], b = tile_s[j0 + 1][d >> 1];
       w[e] = (d & 1) ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
+    }
+    if (kept > 0) {
+      const u32x4 old = dst[i];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t keep = (2 * e + 1 < kept) ? 0xFFFFFFFFu : (2 * e < kept ? 0x0000FFFFu : 0u);
+        w[e] = (old[e] & keep) | (w[e] & ~keep);
+      }
     }
     dst[i] = w;
   }
@@ -116,7 +133,7 @@ hipError_t launch_k_tiles_bf16(const void* k, void* kt, int nseq, int len, int H
   if (nseq <= 0 || len <= 0) return hipSuccess;
   const int ntile = (len + 63) / 64;
   hipLaunchKernelGGL(k_tiles_kernel, dim3((unsigned)ntile, (unsigned)H, (unsigned)nseq), dim3(NT), 0, stream,
-                     (const uint16_t*)k, (u32x4*)kt, len, H, (const f32x2*)table, rope_T);
+                     (const uint16_t*)k, (u32x4*)kt, len, H, (const f32x2*)table, rope_T, 0, ntile);
   return hipGetLastError();
 }
 
@@ -124,7 +141,20 @@ hipError_t launch_v_tiles_bf16(const void* v, void* vt, int nseq, int len, int H
   if (nseq <= 0 || len <= 0) return hipSuccess;
   const int ntile = (len + 63) / 64;
   hipLaunchKernelGGL(v_tiles_kernel, dim3((unsigned)ntile, (unsigned)H, (unsigned)nseq), dim3(NT), 0, stream,
-                     (const uint16_t*)v, (u32x4*)vt, len, H);
+                     (const uint16_t*)v, (u32x4*)vt, len, H, 0, ntile);
+  return hipGetLastError();
+}
+
+hipError_t launch_tiles_append_bf16(const void* k, const void* v, void* kt, void* vt, int dst_ntile, int key0, int n,
+                                    int H, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  const int tiles = (key0 + n - 1) / 64 - key0 / 64 + 1;
+  hipLaunchKernelGGL(k_tiles_kernel, dim3((unsigned)tiles, (unsigned)H, 1u), dim3(NT), 0, stream,
+                     (const uint16_t*)k, (u32x4*)kt, n, H, (const f32x2*)nullptr, 1, key0, dst_ntile);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(v_tiles_kernel, dim3((unsigned)tiles, (unsigned)H, 1u), dim3(NT), 0, stream,
+                     (const uint16_t*)v, (u32x4*)vt, n, H, key0, dst_ntile);
   return hipGetLastError();
 }
 

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define VGGT_ATTN_ABI_VERSION 1
+#define VGGT_ATTN_ABI_VERSION 2
 #define VGGT_HEAD_DIM 64
 
 typedef enum {
@@ -147,6 +147,59 @@ size_t vggt_descriptor_xattn_workspace(int S, int T, int Dn, int H, int kv_split
 vggt_status vggt_descriptor_xattn(const void* q, const void* kd, const void* vd, void* o, vggt_dtype dt, int S,
                                   int T, int Dn, int H, float scale, int kv_splits, void* workspace,
                                   size_t ws_bytes, void* stream);
+
+/*
+ * FlashVGGT chunk-recursive (streaming) descriptor attention (FlashVGGT README,
+ * "Overview": online inference over long sequences reuses the cached
+ * descriptors of earlier chunks; "Key Arguments": --chunksize, frames per
+ * chunk, default 10).  Frames arrive in chunks; after chunk c has been pooled
+ * and appended, the queries of chunk c attend to every descriptor cached so
+ * far (chunks 0..c, own chunk included), in frame order.
+ *
+ * A descriptor cache is caller-owned device memory of
+ * vggt_descriptor_cache_bytes(capacity, H, dt) bytes (256-byte aligned) for up
+ * to `capacity` descriptors of H heads, kept in the layout the attention
+ * kernels read, so that attending to it needs no per-call preparation:
+ *   VGGT_BF16: K and V in 64-descriptor tiles (K rows, V transposed), the
+ *              slots past the last appended descriptor of a tile zeroed;
+ *   VGGT_F32 : K [capacity][H][64] followed by V [capacity][H][64], float32.
+ * Its contents are defined only for the descriptors appended so far; the
+ * caller keeps that count (`used`).  Appends and attention calls on one cache
+ * must be ordered on one stream.
+ */
+size_t vggt_descriptor_cache_bytes(int capacity, int H, vggt_dtype dt);
+
+/*
+ * Append n descriptors (kd, vd [n, H, 64] device, dtype dt: e.g. the output of
+ * vggt_descriptor_pool for a chunk of frames, [S_chunk, Dn, H, 64]) at
+ * positions used .. used+n-1 of the cache.  Requires 0 <= used and
+ * used + n <= capacity (VGGT_ERR_SHAPE otherwise).  Descriptors below `used`
+ * are left as they are; kd/vd must not overlap the cache (VGGT_ERR_ALIAS).
+ */
+vggt_status vggt_descriptor_cache_append(void* cache, vggt_dtype dt, int capacity, int H, int used, const void* kd,
+                                         const void* vd, int n, void* stream);
+
+/*
+ * nq query tokens (q [nq, H, 64]) attend to the first `used` cached
+ * descriptors (1 <= used <= capacity); o [nq, H, 64].  No RoPE inside.
+ * scale and kv_splits as for vggt_global_attn; workspace of at least
+ * vggt_descriptor_cache_attn_workspace(nq, used, H, kv_splits, dt) bytes.
+ * o must not overlap q, the cache or the workspace.
+ */
+size_t vggt_descriptor_cache_attn_workspace(int nq, int used, int H, int kv_splits, vggt_dtype dt);
+vggt_status vggt_descriptor_cache_attn(const void* q, const void* cache, void* o, vggt_dtype dt, int capacity, int H,
+                                       int used, int nq, float scale, int kv_splits, void* workspace,
+                                       size_t ws_bytes, void* stream);
+
+/*
+ * Every chunk at once, in one launch: the cache holds the descriptors of all S
+ * frames (S*Dn <= capacity, appended in frame order from position 0); the
+ * query tokens of frames [c*F, min(S, (c+1)*F)) attend to the descriptors of
+ * frames [0, min(S, (c+1)*F)), F = chunk_frames >= 1.  The result equals S/F
+ * streaming steps.  q, o [S, T, H, 64]; no workspace.
+ */
+vggt_status vggt_descriptor_chunked_xattn(const void* q, const void* cache, void* o, vggt_dtype dt, int capacity,
+                                          int H, int S, int T, int Dn, int chunk_frames, float scale, void* stream);
 
 #ifdef __cplusplus
 }

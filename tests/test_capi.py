@@ -32,7 +32,7 @@ def L():
 
 def test_exports_match_header(L):
     declared = header_functions()
-    assert len(declared) == 12
+    assert len(declared) == 17
     out = subprocess.run(["nm", "-D", "--defined-only", ffv.LIB_PATH], capture_output=True, text=True,
                          check=True).stdout
     exported = sorted(set(m for m in re.findall(r"\bT (vggt_\w+)", out)))
@@ -41,7 +41,7 @@ def test_exports_match_header(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.vggt_abi_version() == 1
+    assert L.vggt_abi_version() == 2
     for code, name in ffv.STATUS.items():
         assert L.vggt_status_str(code).decode() == name
     assert L.vggt_status_str(99).decode() == "VGGT_ERR_UNKNOWN"
@@ -128,3 +128,43 @@ def test_rejects_bad_arguments_without_device(L):
     assert x(_p(A), _p(B), _p(C), _p(O), 0, 2, 8, 0, 1, 0.0, 0, None, 0, None) == SHAPE
     assert x(_p(A), _p(B), _p(C), _p(B), 0, 2, 8, 3, 1, 0.0, 1, None, 0, None) == ALIAS
     assert L.vggt_last_error().decode() != ""
+
+
+def test_descriptor_cache_sizes(L):
+    BF16, F32 = 0, 1
+    # bf16: K tiles and transposed-V tiles of 64 descriptors per head; fp32: plain K then V
+    assert L.vggt_descriptor_cache_bytes(36600, 16, BF16) == 2 * 16 * 572 * 64 * 64 * 2
+    assert L.vggt_descriptor_cache_bytes(65, 2, BF16) == 2 * 2 * 2 * 64 * 64 * 2
+    assert L.vggt_descriptor_cache_bytes(65, 2, F32) == 2 * 65 * 2 * 64 * 4
+    assert L.vggt_descriptor_cache_bytes(0, 16, BF16) == 0
+    assert L.vggt_descriptor_cache_bytes(10, 0, BF16) == 0
+    # attention on the cache needs only split partials
+    assert L.vggt_descriptor_cache_attn_workspace(13740, 3660, 16, 1, BF16) == 0
+    assert L.vggt_descriptor_cache_attn_workspace(1000, 3660, 16, 3, BF16) >= 3 * 1000 * 16 * 66 * 4
+    assert L.vggt_descriptor_cache_attn_workspace(1000, 0, 16, 3, BF16) == 0
+
+
+def test_descriptor_cache_rejects_bad_arguments(L):
+    ap = L.vggt_descriptor_cache_append
+    # (cache, dt, capacity, H, used, kd, vd, n, stream)
+    assert ap(_p(A), 0, 100, 2, 90, _p(B), _p(C), 11, None) == SHAPE   # past capacity
+    assert ap(_p(A), 0, 100, 2, -1, _p(B), _p(C), 1, None) == SHAPE
+    assert ap(_p(A), 0, 100, 2, 0, _p(B), _p(C), 0, None) == OK        # nothing to append
+    assert ap(_p(A), 0, 100, 2, 0, None, _p(C), 5, None) == NULL
+    assert ap(_p(A), 0, 100, 2, 0, _p(B + 4), _p(C), 5, None) == ALIGN
+    assert ap(_p(A), 0, 100, 2, 0, _p(A + 256), _p(C), 5, None) == ALIAS  # kd inside the cache
+    assert ap(_p(A), 5, 100, 2, 0, _p(B), _p(C), 5, None) == UNSUP
+    at = L.vggt_descriptor_cache_attn
+    # (q, cache, o, dt, capacity, H, used, nq, scale, kv_splits, ws, ws_bytes, stream)
+    assert at(_p(B), _p(A), _p(O), 0, 100, 2, 0, 10, 0.0, 0, None, 0, None) == SHAPE    # nothing cached
+    assert at(_p(B), _p(A), _p(O), 0, 100, 2, 101, 10, 0.0, 0, None, 0, None) == SHAPE  # used > capacity
+    assert at(_p(B), _p(A), _p(A), 0, 100, 2, 50, 10, 0.0, 0, None, 0, None) == ALIAS   # o is the cache
+    assert at(_p(B), _p(A), _p(O), 0, 100, 2, 50, 10, 0.0, 65, None, 0, None) == SHAPE
+    assert at(_p(B), _p(A), _p(O), 0, 4000, 2, 3000, 1000, 0.0, 3, None, 0, None) == WS
+    assert at(None, None, None, 0, 100, 2, 50, 0, 0.0, 0, None, 0, None) == OK          # no queries
+    ch = L.vggt_descriptor_chunked_xattn
+    # (q, cache, o, dt, capacity, H, S, T, Dn, chunk_frames, scale, stream)
+    assert ch(_p(B), _p(A), _p(O), 0, 100, 2, 3, 8, 34, 1, 0.0, None) == SHAPE  # 3*34 > capacity
+    assert ch(_p(B), _p(A), _p(O), 0, 100, 2, 3, 8, 30, 0, 0.0, None) == SHAPE  # chunk of zero frames
+    assert ch(None, _p(A), _p(O), 0, 100, 2, 3, 8, 30, 1, 0.0, None) == NULL
+    assert ch(_p(B), _p(A), _p(B), 0, 100, 2, 3, 8, 30, 1, 0.0, None) == ALIAS
