@@ -45,7 +45,11 @@ SIGNATURES = {
     "vggt_descriptor_cache_attn_workspace": (_sz, [_i, _i, _i, _i, _i]),
     "vggt_descriptor_cache_attn": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]),
     "vggt_descriptor_chunked_xattn": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp]),
+    "vggt_timer_start": (_i, [_i]),
+    "vggt_timer_stop": (_i, [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(_i), _i, ctypes.POINTER(_i)]),
 }
+
+TIMER_KINDS = {1: "frame", 2: "global", 3: "xattn", 4: "cache", 5: "chunked"}
 
 _lib = None
 
@@ -313,3 +317,27 @@ class DescriptorCache:
     def attend_chunked(self, q: torch.Tensor, Dn: int, chunk_frames: int, out=None, scale=0.0,
                        stream=None) -> torch.Tensor:
         return vggt_descriptor_chunked_xattn(q, self.buffer, self.capacity, Dn, chunk_frames, out, scale, stream)
+
+
+# ---------------------------------------------------------------------------
+# diagnostics: attention kernel timer
+# ---------------------------------------------------------------------------
+
+_timer_capacity = 0
+
+
+def vggt_timer_start(capacity: int) -> None:
+    """Arm device-side timing of the next `capacity` attention kernel launches."""
+    global _timer_capacity
+    _check("vggt_timer_start", lib().vggt_timer_start(capacity))
+    _timer_capacity = capacity
+
+
+def vggt_timer_stop() -> list[tuple[str, float]]:
+    """Wait for the recorded launches and return [(call kind, kernel ms), ...] in launch order."""
+    n_max = max(_timer_capacity, 1)
+    ms = (ctypes.c_float * n_max)()
+    kinds = (ctypes.c_int * n_max)()
+    n = ctypes.c_int(0)
+    _check("vggt_timer_stop", lib().vggt_timer_stop(ms, kinds, n_max, ctypes.byref(n)))
+    return [(TIMER_KINDS.get(kinds[i], str(kinds[i])), float(ms[i])) for i in range(min(n.value, n_max))]

@@ -124,11 +124,21 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
   xcd_remap(blockIdx.x, nwg, logical);
   const int qt = logical % ntq;
   int rest = logical / ntq;
-  const int head = rest % p.H;
-  rest /= p.H;
-  const int split = rest % p.splits;
-  // with growing key prefixes the longest sequences are started first
-  const int seq = p.nk_step > 0 ? p.nseq - 1 - rest / p.splits : rest / p.splits;
+  int head, split, seq;
+  if (p.nk_step > 0) {
+    // growing key prefixes: each XCD's contiguous range holds whole heads, and
+    // within a head the longest sequences come first (balanced XCDs, long
+    // workgroups dispatched early)
+    seq = p.nseq - 1 - rest % p.nseq;
+    rest /= p.nseq;
+    split = rest % p.splits;
+    head = rest / p.splits;
+  } else {
+    head = rest % p.H;
+    rest /= p.H;
+    split = rest % p.splits;
+    seq = rest / p.splits;
+  }
   const int nq_seq = (int)min((int64_t)p.nq, p.nq_total - (int64_t)seq * p.nq);
   const int nk_seq = p.nk_step > 0 ? (int)min((int64_t)p.nk, (int64_t)(seq + 1) * p.nk_step) : p.nk;
 

@@ -11,6 +11,7 @@
 #include <cstdio>
 #include <cstring>
 #include <mutex>
+#include <vector>
 
 #include "common.h"
 
@@ -121,8 +122,36 @@ SplitPlan plan_splits(int64_t nq, int64_t nk, int H, int requested, vggt_dtype d
   return p;
 }
 
-hipError_t run_attention(const vggt::AttnProblem& p, vggt_dtype dt, hipStream_t st) {
-  hipError_t e = dt == VGGT_F32 ? vggt::launch_attn_f32(p, st) : vggt::launch_attn_bf16(p, st);
+// ---- diagnostics: device-side timing of attention kernel launches (armed by
+//      vggt_timer_start; one timer per process)
+struct KernelTimer {
+  std::mutex mu;
+  bool armed = false;
+  int device = -1;
+  int next = 0;
+  std::vector<hipEvent_t> ev;  // two per slot
+  std::vector<int> kind;
+};
+KernelTimer g_timer;
+
+// Claims the next slot for a launch of `kind` on the current device, or -1.
+int timer_claim(int kind) {
+  std::lock_guard<std::mutex> lk(g_timer.mu);
+  if (!g_timer.armed || g_timer.next >= (int)g_timer.kind.size()) return -1;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != g_timer.device) return -1;
+  g_timer.kind[g_timer.next] = kind;
+  return g_timer.next++;
+}
+
+hipError_t run_attention(const vggt::AttnProblem& p, vggt_dtype dt, hipStream_t st, int kind) {
+  const int slot = timer_claim(kind);
+  hipError_t e = hipSuccess;
+  if (slot >= 0) e = hipEventRecord(g_timer.ev[2 * slot], st);
+  if (e != hipSuccess) return e;
+  e = dt == VGGT_F32 ? vggt::launch_attn_f32(p, st) : vggt::launch_attn_bf16(p, st);
+  if (e != hipSuccess) return e;
+  if (slot >= 0) e = hipEventRecord(g_timer.ev[2 * slot + 1], st);
   if (e != hipSuccess) return e;
   if (p.splits > 1) e = vggt::launch_attn_merge(p, dt == VGGT_BF16, st);
   return e;
@@ -271,7 +300,7 @@ vggt::AttnProblem base_problem(const void* q, const void* k, const void* v, void
 
 // Enqueue the preparation passes and the attention for one call.
 hipError_t run_call(const Layout& L, vggt::AttnProblem p, vggt_dtype dt, int nseq, int64_t nq, int64_t nk,
-                    const int32_t* pos, float base, int rope_T, char* ws, hipStream_t st) {
+                    const int32_t* pos, float base, int rope_T, char* ws, hipStream_t st, int kind) {
   const int H = p.H;
   hipError_t e = hipSuccess;
   if (dt == VGGT_BF16) {
@@ -308,7 +337,7 @@ hipError_t run_call(const Layout& L, vggt::AttnProblem p, vggt_dtype dt, int nse
     p.part_o = (float*)(ws + L.part_o);
     p.part_ml = (float*)(ws + L.part_ml);
   }
-  return run_attention(p, dt, st);
+  return run_attention(p, dt, st, kind);
 }
 
 }  // namespace
@@ -332,7 +361,7 @@ VGGT_API vggt_status vggt_frame_attn(const void* q, const void* k, const void* v
     return s;
   if (vggt_status s = check_device()) return s;
   hipError_t e = run_call(L, base_problem(q, k, v, o, H, scale), dt, S, T, T, pos_yx, rope_base, T,
-                          (char*)workspace, (hipStream_t)stream);
+                          (char*)workspace, (hipStream_t)stream, VGGT_TIMER_FRAME);
   if (e != hipSuccess) return device_error("frame attention launch", e);
   return VGGT_OK;
 }
@@ -359,7 +388,7 @@ VGGT_API vggt_status vggt_global_attn(const void* q, const void* k, const void* 
     return s;
   if (vggt_status s = check_device()) return s;
   hipError_t e = run_call(L, base_problem(q, k, v, o, H, scale), dt, 1, N, N, pos_yx, rope_base, T,
-                          (char*)workspace, (hipStream_t)stream);
+                          (char*)workspace, (hipStream_t)stream, VGGT_TIMER_GLOBAL);
   if (e != hipSuccess) return device_error("global attention launch", e);
   return VGGT_OK;
 }
@@ -423,7 +452,7 @@ VGGT_API vggt_status vggt_descriptor_xattn(const void* q, const void* kd, const 
     return s;
   if (vggt_status s = check_device()) return s;
   hipError_t e = run_call(L, base_problem(q, kd, vd, o, H, scale), dt, 1, nq, nk, nullptr, 0.0f, 1,
-                          (char*)workspace, (hipStream_t)stream);
+                          (char*)workspace, (hipStream_t)stream, VGGT_TIMER_XATTN);
   if (e != hipSuccess) return device_error("descriptor attention launch", e);
   return VGGT_OK;
 }
@@ -550,7 +579,7 @@ VGGT_API vggt_status vggt_descriptor_cache_attn(const void* q, const void* cache
     p.part_o = (float*)((char*)workspace + L.part_o);
     p.part_ml = (float*)((char*)workspace + L.part_ml);
   }
-  hipError_t e = run_attention(p, dt, (hipStream_t)stream);
+  hipError_t e = run_attention(p, dt, (hipStream_t)stream, VGGT_TIMER_CACHE);
   if (e != hipSuccess) return device_error("descriptor cache attention launch", e);
   return VGGT_OK;
 }
@@ -579,7 +608,73 @@ VGGT_API vggt_status vggt_descriptor_chunked_xattn(const void* q, const void* ca
   p.nk_step = F * Dn;
   p.splits = 1;
   p.keys_per_split = (int)pad64(p.nk);
-  hipError_t e = run_attention(p, dt, (hipStream_t)stream);
+  hipError_t e = run_attention(p, dt, (hipStream_t)stream, VGGT_TIMER_CHUNKED);
   if (e != hipSuccess) return device_error("chunked descriptor attention launch", e);
   return VGGT_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Diagnostics: attention kernel timer
+// ---------------------------------------------------------------------------
+
+namespace {
+void timer_release_locked() {
+  for (hipEvent_t e : g_timer.ev)
+    if (e) (void)hipEventDestroy(e);
+  g_timer.ev.clear();
+  g_timer.kind.clear();
+  g_timer.armed = false;
+  g_timer.next = 0;
+  g_timer.device = -1;
+}
+}  // namespace
+
+VGGT_API vggt_status vggt_timer_start(int capacity) {
+  g_last_error[0] = 0;
+  if (capacity < 1 || capacity > (1 << 20)) return fail(VGGT_ERR_SHAPE, "timer capacity must be in [1, 2^20]");
+  std::lock_guard<std::mutex> lk(g_timer.mu);
+  if (g_timer.armed) return fail(VGGT_ERR_SHAPE, "timer already running");
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return device_error("hipGetDevice", e);
+  g_timer.ev.assign(2 * (size_t)capacity, nullptr);
+  for (hipEvent_t& ev : g_timer.ev) {
+    e = hipEventCreate(&ev);
+    if (e != hipSuccess) {
+      ev = nullptr;
+      timer_release_locked();
+      return device_error("hipEventCreate", e);
+    }
+  }
+  g_timer.kind.assign((size_t)capacity, 0);
+  g_timer.device = dev;
+  g_timer.next = 0;
+  g_timer.armed = true;
+  return VGGT_OK;
+}
+
+VGGT_API vggt_status vggt_timer_stop(float* ms, int* kinds, int n_max, int* n_recorded) {
+  g_last_error[0] = 0;
+  std::lock_guard<std::mutex> lk(g_timer.mu);
+  if (!g_timer.armed) return fail(VGGT_ERR_SHAPE, "timer not running");
+  if (n_max < 0 || (n_max > 0 && (!ms || !kinds))) {
+    timer_release_locked();
+    return fail(VGGT_ERR_NULL, "ms and kinds are required when n_max > 0");
+  }
+  vggt_status st = VGGT_OK;
+  const int n = g_timer.next;
+  for (int i = 0; i < n && i < n_max; ++i) {
+    hipError_t e = hipEventSynchronize(g_timer.ev[2 * i + 1]);
+    float t = 0.0f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&t, g_timer.ev[2 * i], g_timer.ev[2 * i + 1]);
+    if (e != hipSuccess) {
+      st = device_error("timer event", e);
+      break;
+    }
+    ms[i] = t;
+    kinds[i] = g_timer.kind[i];
+  }
+  if (n_recorded) *n_recorded = n;
+  timer_release_locked();
+  return st;
 }

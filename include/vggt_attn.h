@@ -201,6 +201,37 @@ vggt_status vggt_descriptor_cache_attn(const void* q, const void* cache, void* o
 vggt_status vggt_descriptor_chunked_xattn(const void* q, const void* cache, void* o, vggt_dtype dt, int capacity,
                                           int H, int S, int T, int Dn, int chunk_frames, float scale, void* stream);
 
+/*
+ * Diagnostics: device-side timing of the attention kernel of each call, for
+ * measuring the kernel on its own (its key-tile preparation, RoPE table and
+ * split-merge passes are not included).  Nothing here is needed to compute.
+ *
+ * vggt_timer_start(capacity) creates 2*capacity HIP events on the current
+ * device and arms the timer: each later attention kernel launch on that
+ * device (by vggt_frame_attn, vggt_global_attn, vggt_descriptor_xattn,
+ * vggt_descriptor_cache_attn or vggt_descriptor_chunked_xattn), up to
+ * `capacity` of them, is bracketed by two events recorded on the call's
+ * stream.  capacity in [1, 2^20]; VGGT_ERR_SHAPE if the timer is already
+ * running.
+ *
+ * vggt_timer_stop(ms, kinds, n_max, n_recorded) waits for the recorded
+ * events, writes the first min(n_max, recorded) durations in milliseconds and
+ * call kinds (vggt_timer_kind) in launch order, stores the number recorded in
+ * *n_recorded (if not NULL), then disarms the timer and destroys its events.
+ * VGGT_ERR_SHAPE if the timer is not running.  One timer per process; calls
+ * made from several threads while it is armed are recorded in the order they
+ * claim a slot.
+ */
+typedef enum {
+  VGGT_TIMER_FRAME = 1,
+  VGGT_TIMER_GLOBAL = 2,
+  VGGT_TIMER_XATTN = 3,
+  VGGT_TIMER_CACHE = 4,
+  VGGT_TIMER_CHUNKED = 5
+} vggt_timer_kind;
+vggt_status vggt_timer_start(int capacity);
+vggt_status vggt_timer_stop(float* ms, int* kinds, int n_max, int* n_recorded);
+
 #ifdef __cplusplus
 }
 #endif

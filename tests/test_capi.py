@@ -32,7 +32,7 @@ def L():
 
 def test_exports_match_header(L):
     declared = header_functions()
-    assert len(declared) == 17
+    assert len(declared) == 19
     out = subprocess.run(["nm", "-D", "--defined-only", ffv.LIB_PATH], capture_output=True, text=True,
                          check=True).stdout
     exported = sorted(set(m for m in re.findall(r"\bT (vggt_\w+)", out)))
@@ -168,3 +168,12 @@ def test_descriptor_cache_rejects_bad_arguments(L):
     assert ch(_p(B), _p(A), _p(O), 0, 100, 2, 3, 8, 30, 0, 0.0, None) == SHAPE  # chunk of zero frames
     assert ch(None, _p(A), _p(O), 0, 100, 2, 3, 8, 30, 1, 0.0, None) == NULL
     assert ch(_p(B), _p(A), _p(B), 0, 100, 2, 3, 8, 30, 1, 0.0, None) == ALIAS
+
+
+def test_timer_arguments(L):
+    # no device work: a stop without a start and bad capacities fail before any HIP call
+    n = ctypes.c_int(-1)
+    assert L.vggt_timer_stop(None, None, 0, ctypes.byref(n)) == SHAPE
+    assert n.value == -1
+    assert L.vggt_timer_start(0) == SHAPE
+    assert L.vggt_timer_start((1 << 20) + 1) == SHAPE

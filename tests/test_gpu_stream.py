@@ -120,3 +120,27 @@ def test_full_size_streaming():
     check_bf16(to_f64(out).reshape(wl.N, H, 64)[rows], ref, f"s100 streaming ({rows.size} rows)")
     oc = cache.attend_chunked(qd, Dn, F)
     check_bf16(to_f64(oc).reshape(wl.N, H, 64)[rows], ref, f"s100 chunked ({rows.size} rows)")
+
+
+def test_kernel_timer_brackets_attention_kernels():
+    wl = workload.Workload("t", 33, S=4, gh=16, gw=16, n_special=5, patch_begin=5, H=4)
+    q, k, v = wl.qkv_bf16()
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    pos = torch.from_numpy(wl.positions()).to(dev())
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ffv.vggt_timer_start(8)
+    a.record(stream)
+    ffv.vggt_global_attn(qd, kd, vd, pos_yx=pos, kv_splits=2)
+    b.record(stream)
+    ffv.vggt_frame_attn(qd, kd, vd, pos_yx=pos)
+    rec = ffv.vggt_timer_stop()
+    assert [kind for kind, _ in rec] == ["global", "frame"]
+    assert all(ms > 0 for _, ms in rec)
+    # the kernel alone takes no longer than the whole call (prep + kernel + merge)
+    assert rec[0][1] <= a.elapsed_time(b) + 1e-3
+    # launches past the capacity are not recorded; the timer can be re-armed
+    ffv.vggt_timer_start(1)
+    ffv.vggt_frame_attn(qd, kd, vd)
+    ffv.vggt_frame_attn(qd, kd, vd)
+    assert [kind for kind, _ in ffv.vggt_timer_stop()] == ["frame"]
