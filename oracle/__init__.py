@@ -48,6 +48,8 @@ def lib():
                                        ctypes.c_int64, ctypes.c_int64, ctypes.c_double, lp, ctypes.c_int64,
                                        ctypes.c_int]
         L.oracle_attention.restype = ctypes.c_int
+        L.oracle_layer_norm.argtypes = [dp, ctypes.c_int64, ctypes.c_int, ctypes.c_int, dp, dp, ctypes.c_double]
+        L.oracle_layer_norm.restype = None
         L.oracle_descriptor_count.argtypes = [ctypes.c_int] * 5
         L.oracle_descriptor_count.restype = ctypes.c_int
         L.oracle_descriptor_pool.argtypes = [dp, dp] + [ctypes.c_int] * 9
@@ -90,6 +92,25 @@ def rope(x: np.ndarray, pos_tok: np.ndarray, base: float) -> np.ndarray:
     return y
 
 
+def layer_norm(x: np.ndarray, gamma, beta, eps: float = 1e-5) -> np.ndarray:
+    """Per-head LayerNorm copy of x [n_tok, H, D] (float64) with gamma/beta [D]."""
+    y = np.array(to_f64(x), dtype=np.float64, order="C", copy=True)
+    n_tok, H, D = y.shape
+    g = np.ascontiguousarray(to_f64(gamma), dtype=np.float64).reshape(D)
+    b = np.ascontiguousarray(to_f64(beta), dtype=np.float64).reshape(D)
+    lib().oracle_layer_norm(_dp(y), n_tok, H, D, _dp(g), _dp(b), float(eps))
+    return y
+
+
+def _prologue(x, pos, base, norm, S):
+    """Q/K prologue: optional per-head LayerNorm (gamma, beta, eps), then RoPE."""
+    if norm is not None:
+        x = layer_norm(x, norm[0], norm[1], norm[2])
+    if pos is not None:
+        x = rope(x, _frame_positions(pos, S), base)
+    return x
+
+
 def attention(q, k, v, *, group_q: int = 0, group_k: int = 0, scale: float | None = None, rows=None,
               nthreads: int | None = None) -> np.ndarray:
     """Multi-head softmax attention.  q [nq, H, D], k/v [nk, H, D] (any of
@@ -120,26 +141,25 @@ def _frame_positions(pos: np.ndarray, S: int) -> np.ndarray:
     return np.tile(np.asarray(pos, dtype=np.int32).reshape(-1, 2), (S, 1))
 
 
-def frame_attn(q, k, v, S: int, T: int, pos=None, base: float = 100.0, scale=None, rows=None, nthreads=None):
+def frame_attn(q, k, v, S: int, T: int, pos=None, base: float = 100.0, scale=None, rows=None, nthreads=None,
+               q_norm=None, k_norm=None):
     """Frame-wise attention: S independent sequences of T tokens.
-    q/k/v [S, T, H, D]; pos [T, 2] shared by all frames (None: no RoPE).
+    q/k/v [S, T, H, D]; pos [T, 2] shared by all frames (None: no RoPE);
+    q_norm/k_norm (gamma, beta, eps) or None: per-head LayerNorm before RoPE.
     rows index tokens of the flattened [S*T] axis."""
     H, D = q.shape[-2:]
     qf, kf, vf = (to_f64(x).reshape(S * T, H, D) for x in (q, k, v))
-    if pos is not None:
-        pt = _frame_positions(pos, S)
-        qf, kf = rope(qf, pt, base), rope(kf, pt, base)
+    qf, kf = _prologue(qf, pos, base, q_norm, S), _prologue(kf, pos, base, k_norm, S)
     return attention(qf, kf, vf, group_q=T, group_k=T, scale=scale, rows=rows, nthreads=nthreads)
 
 
-def global_attn(q, k, v, S: int, T: int, pos=None, base: float = 100.0, scale=None, rows=None, nthreads=None):
+def global_attn(q, k, v, S: int, T: int, pos=None, base: float = 100.0, scale=None, rows=None, nthreads=None,
+                q_norm=None, k_norm=None):
     """Global attention: one sequence of S*T tokens; each token keeps its own
-    within-frame (row, col) position for RoPE."""
+    within-frame (row, col) position for RoPE.  q_norm/k_norm as for frame_attn."""
     H, D = q.shape[-2:]
     qf, kf, vf = (to_f64(x).reshape(S * T, H, D) for x in (q, k, v))
-    if pos is not None:
-        pt = _frame_positions(pos, S)
-        qf, kf = rope(qf, pt, base), rope(kf, pt, base)
+    qf, kf = _prologue(qf, pos, base, q_norm, S), _prologue(kf, pos, base, k_norm, S)
     return attention(qf, kf, vf, scale=scale, rows=rows, nthreads=nthreads)
 
 

@@ -88,6 +88,37 @@ void oracle_rope(double* x, int64_t n_tok, int H, int D, const int32_t* pos_yx, 
 }
 
 /* ------------------------------------------------------------------------ */
+/* Per-head LayerNorm of Q and K                                            */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Centered LayerNorm over the D channels of every head vector, in place
+ * (VGGT-JAX README, kernel-trial table: LayerNorm on the Q/K shapes, the
+ * existing centered LayerNorm kept; VGGT-Omega-1B-512-bf16 config article,
+ * model-structure section: layer_norm_eps 1e-05):
+ *   mu     = mean_c u_c
+ *   var    = mean_c (u_c - mu)^2              (biased)
+ *   u'_c   = (u_c - mu) / sqrt(var + eps) * gamma_c + beta_c
+ *   x      [n_tok][H][D] float64; gamma, beta [D] float64, shared by the heads.
+ */
+void oracle_layer_norm(double* x, int64_t n_tok, int H, int D, const double* gamma, const double* beta,
+                       double eps) {
+  for (int64_t t = 0; t < n_tok; ++t) {
+    for (int h = 0; h < H; ++h) {
+      double* u = x + (t * H + h) * (int64_t)D;
+      double mu = 0.0;
+      for (int c = 0; c < D; ++c) mu += u[c];
+      mu /= D;
+      double var = 0.0;
+      for (int c = 0; c < D; ++c) var += (u[c] - mu) * (u[c] - mu);
+      var /= D;
+      const double inv = 1.0 / sqrt(var + eps);
+      for (int c = 0; c < D; ++c) u[c] = (u[c] - mu) * inv * gamma[c] + beta[c];
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Scaled dot-product attention, multi-head                                 */
 /* ------------------------------------------------------------------------ */
 

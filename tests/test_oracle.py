@@ -292,6 +292,75 @@ def test_frame_vs_global_consistency_and_row_sampling():
 
 
 # --------------------------------------------------------------------------
+# Per-head Q/K LayerNorm
+# --------------------------------------------------------------------------
+
+def _torch_layer_norm(x, g, b, eps):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float64))
+    return torch.nn.functional.layer_norm(t, (x.shape[-1],), torch.from_numpy(np.asarray(g, np.float64)),
+                                          torch.from_numpy(np.asarray(b, np.float64)), eps).numpy()
+
+
+def test_layer_norm_against_library_routine():
+    r = _rng(40)
+    x = r.standard_normal((7, 3, 64)) * 3.0 + 1.5
+    g, b = r.standard_normal(64), r.standard_normal(64)
+    for eps in (1e-5, 0.5):
+        np.testing.assert_allclose(oracle.layer_norm(x, g, b, eps), _torch_layer_norm(x, g, b, eps),
+                                   rtol=1e-12, atol=1e-13)
+
+
+def test_layer_norm_closed_forms():
+    r = _rng(41)
+    g, b = r.standard_normal(64), r.standard_normal(64)
+    # a constant head vector has no deviation: the output is beta
+    np.testing.assert_array_equal(oracle.layer_norm(np.full((2, 2, 64), 3.25), g, b, 1e-5)[0, 1], b)
+    x = r.standard_normal((5, 2, 64))
+    ones, zeros = np.ones(64), np.zeros(64)
+    y = oracle.layer_norm(x, ones, zeros, 0.0)
+    np.testing.assert_allclose(y.mean(axis=-1), 0.0, atol=1e-14)
+    np.testing.assert_allclose((y ** 2).mean(axis=-1), 1.0, rtol=1e-13)
+    # invariant under positive scaling and shifting of the input (eps = 0)
+    np.testing.assert_allclose(oracle.layer_norm(2.5 * x - 7.0, g, b, 0.0), oracle.layer_norm(x, g, b, 0.0),
+                               rtol=1e-12, atol=1e-12)
+    # eps shrinks the normalised deviation by sqrt(var / (var + eps))
+    var = x.var(axis=-1, keepdims=True)
+    y_eps = oracle.layer_norm(x, ones, zeros, 0.3)
+    np.testing.assert_allclose(y_eps, y * np.sqrt(var / (var + 0.3)), rtol=1e-12, atol=1e-14)
+
+
+def test_attention_with_qk_norm_brute_force():
+    wl = workload.Workload("t", 11, S=2, gh=3, gw=4, n_special=2, patch_begin=2, H=2, D=64)
+    q, k, v = (x.astype(np.float64) for x in wl.qkv_f32())
+    r = _rng(42)
+    qn = (r.standard_normal(64), r.standard_normal(64), 1e-5)
+    kn = (r.standard_normal(64), r.standard_normal(64), 1e-5)
+    pos = wl.positions()
+    S, T = wl.S, wl.T
+    pt = np.tile(pos, (S, 1))
+    qr = _einsum_rope(_torch_layer_norm(q.reshape(S * T, 2, 64), *qn), pt, 100.0)
+    kr = _einsum_rope(_torch_layer_norm(k.reshape(S * T, 2, 64), *kn), pt, 100.0)
+    vv = v.reshape(S * T, 2, 64)
+    got = oracle.global_attn(q, k, v, S, T, pos=pos, q_norm=qn, k_norm=kn)
+    np.testing.assert_allclose(got, _einsum_attention(qr, kr, vv, 0.125), rtol=1e-11, atol=1e-13)
+    f = oracle.frame_attn(q, k, v, S, T, pos=pos, q_norm=qn, k_norm=kn)
+    ref = np.concatenate([_einsum_attention(qr[s * T:(s + 1) * T], kr[s * T:(s + 1) * T], vv[s * T:(s + 1) * T],
+                                            0.125) for s in range(S)])
+    np.testing.assert_allclose(f, ref, rtol=1e-11, atol=1e-13)
+
+
+def test_qk_norm_with_zero_gain_makes_keys_identical():
+    # gamma = 0 maps every key to beta: no RoPE, so the output averages the values
+    wl = workload.Workload("t", 12, S=2, gh=3, gw=3, n_special=1, patch_begin=0, H=1, D=64)
+    q, k, v = wl.qkv_bf16()
+    beta = _rng(43).standard_normal(64)
+    got = oracle.global_attn(q, k, v, wl.S, wl.T, k_norm=(np.zeros(64), beta, 1e-5))
+    vm = oracle.to_f64(v).reshape(-1, 1, 64).mean(axis=0)
+    np.testing.assert_allclose(got, np.broadcast_to(vm, got.shape), rtol=1e-12, atol=1e-14)
+
+
+# --------------------------------------------------------------------------
 # Descriptor pooling and cross-attention
 # --------------------------------------------------------------------------
 
