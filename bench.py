@@ -219,6 +219,7 @@ def main() -> int:
         "input_gen_s": round(gen_s, 2),
     }
 
+    result["qknorm"] = bench_qknorm(ffv, qd, kd, vd, posd, go, fo, ws_g, ws_f, max(3, args.steps // 2), flops)
     if not args.no_stream:
         result["stream"] = bench_stream(ffv, dev, max(3, args.steps // 2), 2)
     if not args.no_cpu_baseline:
@@ -226,6 +227,45 @@ def main() -> int:
                                                                        args.cpu_row_stride)
     print(json.dumps(result), flush=True)
     return 0
+
+
+def bench_qknorm(ffv, qd, kd, vd, posd, go, fo, ws_g, ws_f, iters, flops):
+    """Frame and global attention of the same workload with the fused per-head
+    Q/K LayerNorm + RoPE prologue (seeded gamma/beta around (1, 0))."""
+    import torch
+
+    import workload
+
+    dev = qd.device
+    prm = [torch.from_numpy(workload.normal_f32(0x1A7E + i, (64,)) * 0.3 + (1.0 if i % 2 == 0 else 0.0)).to(dev)
+           for i in range(4)]
+    qn, kn = (prm[0], prm[1]), (prm[2], prm[3])
+    stream = torch.cuda.current_stream()
+
+    def call(kind):
+        if kind == "frame":
+            ffv.vggt_frame_attn_qknorm(qd, kd, vd, qn, kn, out=fo, pos_yx=posd, workspace=ws_f)
+        else:
+            ffv.vggt_global_attn_qknorm(qd, kd, vd, qn, kn, out=go, pos_yx=posd, workspace=ws_g)
+
+    out = {}
+    for kind in ("frame", "global"):
+        for _ in range(2):
+            call(kind)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+        torch.cuda.synchronize()
+        ffv.vggt_timer_start(iters)
+        for a, b in ev:
+            a.record(stream)
+            call(kind)
+            b.record(stream)
+        torch.cuda.synchronize()
+        kern = [ms for _, ms in ffv.vggt_timer_stop()]
+        call_ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+        out[f"{kind}_call_ms"] = round(call_ms, 4)
+        out[f"{kind}_kernel_ms"] = round(float(np.mean(kern)), 4)
+        out[f"{kind}_call_tflops"] = round(flops[kind] / (call_ms * 1e-3) / 1e12, 2)
+    return out
 
 
 def bench_stream(ffv, dev, passes, warmup, chunk_frames=10):

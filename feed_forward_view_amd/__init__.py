@@ -25,8 +25,18 @@ STATUS = {
     5: "VGGT_ERR_ALIAS", 6: "VGGT_ERR_WORKSPACE", 7: "VGGT_ERR_DEVICE",
 }
 
+PRE_ROPE, PRE_QKNORM = 1, 2
+
+
+class QkNorm(ctypes.Structure):
+    """vggt_qk_norm: device pointers of the [64] float32 LayerNorm parameters and eps."""
+    _fields_ = [("q_gamma", ctypes.c_void_p), ("q_beta", ctypes.c_void_p), ("k_gamma", ctypes.c_void_p),
+                ("k_beta", ctypes.c_void_p), ("eps", ctypes.c_float)]
+
+
 # name -> (restype, argtypes); pointers are passed as c_void_p
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_np = ctypes.POINTER(QkNorm)
 SIGNATURES = {
     "vggt_abi_version": (_i, []),
     "vggt_status_str": (ctypes.c_char_p, [_i]),
@@ -36,6 +46,8 @@ SIGNATURES = {
     "vggt_frame_attn": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _f, _f, _vp, _sz, _vp]),
     "vggt_global_attn_workspace": (_sz, [_i, _i, _i, _i, _i, _i]),
     "vggt_global_attn": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _f, _f, _i, _vp, _sz, _vp]),
+    "vggt_frame_attn_qknorm": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _f, _f, _np, _vp, _sz, _vp]),
+    "vggt_global_attn_qknorm": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _f, _f, _i, _np, _vp, _sz, _vp]),
     "vggt_descriptor_count": (_i, [_i, _i, _i, _i, _i]),
     "vggt_descriptor_pool": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i, _vp]),
     "vggt_descriptor_xattn_workspace": (_sz, [_i, _i, _i, _i, _i, _i]),
@@ -138,7 +150,8 @@ def vggt_attn_rope(x: torch.Tensor, pos_yx: torch.Tensor, rope_base: float = 100
 
 
 def vggt_frame_attn_workspace(S, T, H, rope_on, dtype=torch.bfloat16) -> int:
-    return int(lib().vggt_frame_attn_workspace(S, T, H, int(bool(rope_on)), BF16 if dtype == torch.bfloat16 else F32))
+    """rope_on: bool, or PRE_ROPE | PRE_QKNORM flags."""
+    return int(lib().vggt_frame_attn_workspace(S, T, H, int(rope_on), BF16 if dtype == torch.bfloat16 else F32))
 
 
 def vggt_frame_attn(q, k, v, out=None, pos_yx=None, rope_base=100.0, scale=0.0, workspace=None, stream=None):
@@ -159,7 +172,8 @@ def vggt_frame_attn(q, k, v, out=None, pos_yx=None, rope_base=100.0, scale=0.0, 
 
 
 def vggt_global_attn_workspace(S, T, H, kv_splits, rope_on, dtype=torch.bfloat16) -> int:
-    return int(lib().vggt_global_attn_workspace(S, T, H, kv_splits, int(bool(rope_on)),
+    """rope_on: bool, or PRE_ROPE | PRE_QKNORM flags."""
+    return int(lib().vggt_global_attn_workspace(S, T, H, kv_splits, int(rope_on),
                                                 BF16 if dtype == torch.bfloat16 else F32))
 
 
@@ -178,6 +192,58 @@ def vggt_global_attn(q, k, v, out=None, pos_yx=None, rope_base=100.0, scale=0.0,
     _check("vggt_global_attn",
            lib().vggt_global_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _dtype_code(q), S, T, H, _pos(pos_yx, T),
                                   rope_base, scale, kv_splits, _ptr(ws), nbytes, _stream(stream)))
+    return out
+
+
+def _qk_norm(q_norm, k_norm, eps: float, H: int):
+    """QkNorm from (gamma, beta) pairs of float32 [64] GPU tensors."""
+    ptrs = []
+    for name, pair in (("q_norm", q_norm), ("k_norm", k_norm)):
+        for t in pair:
+            if t.dtype != torch.float32 or t.numel() != HEAD_DIM or not t.is_contiguous() or t.device.type != "cuda":
+                raise ValueError(f"{name} gamma/beta must be contiguous float32 GPU tensors of {HEAD_DIM}")
+            ptrs.append(t.data_ptr())
+    return QkNorm(ptrs[0], ptrs[1], ptrs[2], ptrs[3], eps)
+
+
+def _check_qkv(q, k, v, out):
+    S, T, H = _tok(q, "q")
+    for n, t in (("k", k), ("v", v)):
+        if _tok(t, n) != (S, T, H) or t.dtype != q.dtype:
+            raise ValueError(f"{n} must match q")
+    out = torch.empty_like(q) if out is None else out
+    if _tok(out, "out") != (S, T, H) or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    return S, T, H, out
+
+
+def vggt_frame_attn_qknorm(q, k, v, q_norm, k_norm, eps=1e-5, out=None, pos_yx=None, rope_base=100.0, scale=0.0,
+                           workspace=None, stream=None):
+    """Frame-wise attention with per-head LayerNorm of q and k (gamma, beta pairs) before RoPE."""
+    S, T, H, out = _check_qkv(q, k, v, out)
+    norm = _qk_norm(q_norm, k_norm, eps, H)
+    flags = PRE_QKNORM | (PRE_ROPE if pos_yx is not None else 0)
+    need = vggt_frame_attn_workspace(S, T, H, flags, q.dtype)
+    ws, nbytes = _workspace(need, q.device, workspace)
+    _check("vggt_frame_attn_qknorm",
+           lib().vggt_frame_attn_qknorm(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _dtype_code(q), S, T, H,
+                                        _pos(pos_yx, T), rope_base, scale, ctypes.byref(norm), _ptr(ws), nbytes,
+                                        _stream(stream)))
+    return out
+
+
+def vggt_global_attn_qknorm(q, k, v, q_norm, k_norm, eps=1e-5, out=None, pos_yx=None, rope_base=100.0, scale=0.0,
+                            kv_splits=0, workspace=None, stream=None):
+    """Global attention with per-head LayerNorm of q and k (gamma, beta pairs) before RoPE."""
+    S, T, H, out = _check_qkv(q, k, v, out)
+    norm = _qk_norm(q_norm, k_norm, eps, H)
+    flags = PRE_QKNORM | (PRE_ROPE if pos_yx is not None else 0)
+    need = vggt_global_attn_workspace(S, T, H, kv_splits, flags, q.dtype)
+    ws, nbytes = _workspace(need, q.device, workspace)
+    _check("vggt_global_attn_qknorm",
+           lib().vggt_global_attn_qknorm(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _dtype_code(q), S, T, H,
+                                         _pos(pos_yx, T), rope_base, scale, kv_splits, ctypes.byref(norm), _ptr(ws),
+                                         nbytes, _stream(stream)))
     return out
 
 

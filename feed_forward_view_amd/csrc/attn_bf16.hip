@@ -172,7 +172,8 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
     if (i < ntiles) issue(i, i);
 
   // ---- Q fragments (B operand of S^T = K Q^T): lane holds query q0+32*qb+l32,
-  //      dims 16*dc + 8*hi .. +7, rotated and scaled by scale*log2(e).
+  //      dims 16*dc + 8*hi .. +7 (the other 32 dims sit in lane ^ 32), after an
+  //      optional per-head LayerNorm, rotated and scaled by scale*log2(e).
   bf16x8 qf[2][4];
   {
     const f32x2* __restrict__ tab = p.rope_tab;
@@ -183,30 +184,60 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
       const int qrow = ok ? qi : 0;
       const int tpos = tab ? (int)((seq * p.q_seq_stride + qrow) % p.rope_T) : 0;
       const f32x2* trow = tab ? tab + tpos * 32 + 4 * hi : nullptr;
+      float x[4][4], y[4][4];  // [dc][pair]: channels 16dc + 8hi + 2e, +1
 #pragma unroll
       for (int dc = 0; dc < 4; ++dc) {
         u32x4 w = *(const u32x4*)(qg + (int64_t)qrow * p.tok_stride + 16 * dc + 8 * hi);
         if (!ok) w = u32x4{0u, 0u, 0u, 0u};
-        float x[4], y[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          x[e] = lo_bf16(w[e]);
-          y[e] = hi_bf16(w[e]);
+          x[dc][e] = lo_bf16(w[e]);
+          y[dc][e] = hi_bf16(w[e]);
         }
+      }
+      if (p.q_ln_g) {
+        float sum = 0.0f;
+#pragma unroll
+        for (int dc = 0; dc < 4; ++dc)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sum += x[dc][e] + y[dc][e];
+        sum += __shfl_xor(sum, 32);
+        const float mu = sum * (1.0f / D);
+        float dev = 0.0f;
+#pragma unroll
+        for (int dc = 0; dc < 4; ++dc)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            dev = __builtin_fmaf(x[dc][e] - mu, x[dc][e] - mu, dev);
+            dev = __builtin_fmaf(y[dc][e] - mu, y[dc][e] - mu, dev);
+          }
+        dev += __shfl_xor(dev, 32);
+        const float inv = 1.0f / __builtin_sqrtf(dev * (1.0f / D) + p.ln_eps);
+#pragma unroll
+        for (int dc = 0; dc < 4; ++dc)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int c = 16 * dc + 8 * hi + 2 * e;
+            x[dc][e] = __builtin_fmaf((x[dc][e] - mu) * inv, p.q_ln_g[c], p.q_ln_b[c]);
+            y[dc][e] = __builtin_fmaf((y[dc][e] - mu) * inv, p.q_ln_g[c + 1], p.q_ln_b[c + 1]);
+          }
+      }
+#pragma unroll
+      for (int dc = 0; dc < 4; ++dc) {
         if (trow) {
           // pairs 8*dc + 4*hi + e of the 32 rotation pairs of this position
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const f32x2 cs = trow[8 * dc + e];
-            const float x2 = __builtin_fmaf(x[e], cs[0], -y[e] * cs[1]);
-            const float y2 = __builtin_fmaf(x[e], cs[1], y[e] * cs[0]);
-            x[e] = x2;
-            y[e] = y2;
+            const float x2 = __builtin_fmaf(x[dc][e], cs[0], -y[dc][e] * cs[1]);
+            const float y2 = __builtin_fmaf(x[dc][e], cs[1], y[dc][e] * cs[0]);
+            x[dc][e] = x2;
+            y[dc][e] = y2;
           }
         }
         u32x4 r;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) r[e] = pack_bf16x2(x[e] * p.scale_log2, y[e] * p.scale_log2);
+        for (int e = 0; e < 4; ++e) r[e] = pack_bf16x2(x[dc][e] * p.scale_log2, y[dc][e] * p.scale_log2);
         qf[qb][dc] = __builtin_bit_cast(bf16x8, r);
       }
     }

@@ -262,7 +262,7 @@ void add(Layout& L, size_t& off, size_t bytes) {
 // bf16: RoPE table plus K and V^T in 64-key tile layout; fp32: rotated copies
 // of Q and K.  Both: split partials.  Offsets are 256-byte aligned.
 Layout plan(int nseq, int64_t nq, int64_t nk, int H, int rope_T, bool rope_on, bool allow_split, int kv_splits,
-            vggt_dtype dt) {
+            vggt_dtype dt, bool norm_on = false) {
   Layout L;
   const size_t es = elem_size(dt);
   if (dt == VGGT_BF16) {
@@ -274,7 +274,7 @@ Layout plan(int nseq, int64_t nq, int64_t nk, int H, int rope_T, bool rope_on, b
     const size_t tiles_bytes = (size_t)nseq * H * L.ktiles * 64 * vggt::kHeadDim * 2;
     add(L, L.kt, tiles_bytes);
     add(L, L.vt, tiles_bytes);
-  } else if (rope_on) {
+  } else if (rope_on || norm_on) {
     L.use_qr = true;
     add(L, L.qr, (size_t)nseq * nq * H * vggt::kHeadDim * es);
     L.use_kr = true;
@@ -300,10 +300,16 @@ vggt::AttnProblem base_problem(const void* q, const void* k, const void* v, void
 
 // Enqueue the preparation passes and the attention for one call.
 hipError_t run_call(const Layout& L, vggt::AttnProblem p, vggt_dtype dt, int nseq, int64_t nq, int64_t nk,
-                    const int32_t* pos, float base, int rope_T, char* ws, hipStream_t st, int kind) {
+                    const int32_t* pos, float base, int rope_T, char* ws, hipStream_t st, int kind,
+                    const vggt_qk_norm* norm = nullptr) {
   const int H = p.H;
   hipError_t e = hipSuccess;
   if (dt == VGGT_BF16) {
+    if (norm) {
+      p.q_ln_g = norm->q_gamma;
+      p.q_ln_b = norm->q_beta;
+      p.ln_eps = norm->eps;
+    }
     const void* table = nullptr;
     if (L.use_table) {
       e = vggt::launch_rope_table(pos, rope_T, (double)base, ws + L.table, st);
@@ -312,16 +318,33 @@ hipError_t run_call(const Layout& L, vggt::AttnProblem p, vggt_dtype dt, int nse
       p.rope_tab = (const vggt::f32x2*)table;
       p.rope_T = rope_T;
     }
-    e = vggt::launch_k_tiles_bf16(p.k, ws + L.kt, nseq, (int)nk, H, table, rope_T, st);
+    e = vggt::launch_k_tiles_bf16(p.k, ws + L.kt, nseq, (int)nk, H, table, rope_T, norm ? norm->k_gamma : nullptr,
+                                  norm ? norm->k_beta : nullptr, norm ? norm->eps : 0.0f, st);
     if (e == hipSuccess) e = vggt::launch_v_tiles_bf16(p.v, ws + L.vt, nseq, (int)nk, H, st);
     if (e != hipSuccess) return e;
     p.k = ws + L.kt;
     p.vt = ws + L.vt;
     p.ktiles_seq = L.ktiles;
   } else if (L.use_qr) {
-    e = vggt::launch_rope(p.q, ws + L.qr, false, (int64_t)nseq * nq, rope_T, H, pos, (double)base, st);
-    if (e == hipSuccess) e = vggt::launch_rope(p.k, ws + L.kr, false, (int64_t)nseq * nk, rope_T, H, pos, (double)base, st);
-    if (e != hipSuccess) return e;
+    // fp32: LayerNorm and/or RoPE into the rotated copies
+    const int64_t nqt = (int64_t)nseq * nq, nkt = (int64_t)nseq * nk;
+    const void* qs = p.q;
+    const void* ks = p.k;
+    if (norm) {
+      e = vggt::launch_layer_norm_f32((const float*)p.q, (float*)(ws + L.qr), nqt, H, norm->q_gamma, norm->q_beta,
+                                      norm->eps, st);
+      if (e == hipSuccess)
+        e = vggt::launch_layer_norm_f32((const float*)p.k, (float*)(ws + L.kr), nkt, H, norm->k_gamma, norm->k_beta,
+                                        norm->eps, st);
+      if (e != hipSuccess) return e;
+      qs = ws + L.qr;
+      ks = ws + L.kr;
+    }
+    if (pos) {
+      e = vggt::launch_rope(qs, ws + L.qr, false, nqt, rope_T, H, pos, (double)base, st);
+      if (e == hipSuccess) e = vggt::launch_rope(ks, ws + L.kr, false, nkt, rope_T, H, pos, (double)base, st);
+      if (e != hipSuccess) return e;
+    }
     p.q = ws + L.qr;
     p.k = ws + L.kr;
   }
@@ -345,52 +368,110 @@ hipError_t run_call(const Layout& L, vggt::AttnProblem p, vggt_dtype dt, int nse
 VGGT_API size_t vggt_frame_attn_workspace(int S, int T, int H, int rope_on, vggt_dtype dt) {
   if (!dtype_ok(dt) || !tokens_ok(S, T, H)) return 0;
   if (S == 0) return 0;
-  return plan(S, T, T, H, T, rope_on != 0, false, 1, dt).total;
+  return plan(S, T, T, H, T, (rope_on & VGGT_PRE_ROPE) != 0, false, 1, dt, (rope_on & VGGT_PRE_QKNORM) != 0).total;
 }
+
+namespace {
+
+vggt_status check_norm(const vggt_qk_norm* n) {
+  if (!n) return VGGT_OK;
+  if (!n->q_gamma || !n->q_beta || !n->k_gamma || !n->k_beta)
+    return fail(VGGT_ERR_NULL, "q/k LayerNorm gamma and beta are required");
+  if (((reinterpret_cast<uintptr_t>(n->q_gamma) | reinterpret_cast<uintptr_t>(n->q_beta) |
+        reinterpret_cast<uintptr_t>(n->k_gamma) | reinterpret_cast<uintptr_t>(n->k_beta)) & 3u) != 0)
+    return fail(VGGT_ERR_ALIGN, "LayerNorm parameters must be 4-byte aligned");
+  if (!(n->eps > 0.0f) || !std::isfinite(n->eps)) return fail(VGGT_ERR_SHAPE, "LayerNorm eps must be finite and > 0");
+  return VGGT_OK;
+}
+
+// The LayerNorm parameters are read while o and the workspace are written.
+vggt_status check_norm_alias(const vggt_qk_norm* n, const void* o, size_t o_bytes, const void* ws, size_t ws_need) {
+  if (!n) return VGGT_OK;
+  const size_t pb = vggt::kHeadDim * sizeof(float);
+  for (const float* a : {n->q_gamma, n->q_beta, n->k_gamma, n->k_beta})
+    if (overlap(a, pb, o, o_bytes) || overlap(a, pb, ws, ws_need))
+      return fail(VGGT_ERR_ALIAS, "LayerNorm parameters overlap the output or the workspace");
+  return VGGT_OK;
+}
+
+vggt_status frame_attn(const void* q, const void* k, const void* v, void* o, vggt_dtype dt, int S, int T, int H,
+                       const int32_t* pos_yx, float rope_base, float scale, const vggt_qk_norm* norm, void* workspace,
+                       size_t ws_bytes, void* stream) {
+  g_last_error[0] = 0;
+  if (!dtype_ok(dt)) return fail(VGGT_ERR_UNSUPPORTED, "unknown dtype %d", (int)dt);
+  if (!tokens_ok(S, T, H)) return fail(VGGT_ERR_SHAPE, "bad shape S=%d T=%d H=%d", S, T, H);
+  if (vggt_status s = check_norm(norm)) return s;
+  if (S == 0) return VGGT_OK;
+  const size_t bytes = (size_t)S * T * H * vggt::kHeadDim * elem_size(dt);
+  const Layout L = plan(S, T, T, H, T, pos_yx != nullptr, false, 1, dt, norm != nullptr);
+  if (vggt_status s = validate_attn({q, k, v, o}, pos_yx, rope_base, L.total, workspace, ws_bytes, bytes, bytes))
+    return s;
+  if (vggt_status s = check_norm_alias(norm, o, bytes, workspace, L.total)) return s;
+  if (vggt_status s = check_device()) return s;
+  hipError_t e = run_call(L, base_problem(q, k, v, o, H, scale), dt, S, T, T, pos_yx, rope_base, T,
+                          (char*)workspace, (hipStream_t)stream, VGGT_TIMER_FRAME, norm);
+  if (e != hipSuccess) return device_error("frame attention launch", e);
+  return VGGT_OK;
+}
+
+vggt_status global_attn(const void* q, const void* k, const void* v, void* o, vggt_dtype dt, int S, int T, int H,
+                        const int32_t* pos_yx, float rope_base, float scale, int kv_splits, const vggt_qk_norm* norm,
+                        void* workspace, size_t ws_bytes, void* stream) {
+  g_last_error[0] = 0;
+  if (!dtype_ok(dt)) return fail(VGGT_ERR_UNSUPPORTED, "unknown dtype %d", (int)dt);
+  if (!tokens_ok(S, T, H)) return fail(VGGT_ERR_SHAPE, "bad shape S=%d T=%d H=%d", S, T, H);
+  if (kv_splits < 0 || kv_splits > kMaxSplits) return fail(VGGT_ERR_SHAPE, "kv_splits must be in [0, %d]", kMaxSplits);
+  if (vggt_status s = check_norm(norm)) return s;
+  if (S == 0) return VGGT_OK;
+  const int64_t N = (int64_t)S * T;
+  const size_t bytes = (size_t)N * H * vggt::kHeadDim * elem_size(dt);
+  const Layout L = plan(1, N, N, H, T, pos_yx != nullptr, true, kv_splits, dt, norm != nullptr);
+  if (vggt_status s = validate_attn({q, k, v, o}, pos_yx, rope_base, L.total, workspace, ws_bytes, bytes, bytes))
+    return s;
+  if (vggt_status s = check_norm_alias(norm, o, bytes, workspace, L.total)) return s;
+  if (vggt_status s = check_device()) return s;
+  hipError_t e = run_call(L, base_problem(q, k, v, o, H, scale), dt, 1, N, N, pos_yx, rope_base, T,
+                          (char*)workspace, (hipStream_t)stream, VGGT_TIMER_GLOBAL, norm);
+  if (e != hipSuccess) return device_error("global attention launch", e);
+  return VGGT_OK;
+}
+
+}  // namespace
 
 VGGT_API vggt_status vggt_frame_attn(const void* q, const void* k, const void* v, void* o, vggt_dtype dt, int S,
                                      int T, int H, const int32_t* pos_yx, float rope_base, float scale,
                                      void* workspace, size_t ws_bytes, void* stream) {
-  g_last_error[0] = 0;
-  if (!dtype_ok(dt)) return fail(VGGT_ERR_UNSUPPORTED, "unknown dtype %d", (int)dt);
-  if (!tokens_ok(S, T, H)) return fail(VGGT_ERR_SHAPE, "bad shape S=%d T=%d H=%d", S, T, H);
-  if (S == 0) return VGGT_OK;
-  const size_t bytes = (size_t)S * T * H * vggt::kHeadDim * elem_size(dt);
-  const Layout L = plan(S, T, T, H, T, pos_yx != nullptr, false, 1, dt);
-  if (vggt_status s = validate_attn({q, k, v, o}, pos_yx, rope_base, L.total, workspace, ws_bytes, bytes, bytes))
-    return s;
-  if (vggt_status s = check_device()) return s;
-  hipError_t e = run_call(L, base_problem(q, k, v, o, H, scale), dt, S, T, T, pos_yx, rope_base, T,
-                          (char*)workspace, (hipStream_t)stream, VGGT_TIMER_FRAME);
-  if (e != hipSuccess) return device_error("frame attention launch", e);
-  return VGGT_OK;
+  return frame_attn(q, k, v, o, dt, S, T, H, pos_yx, rope_base, scale, nullptr, workspace, ws_bytes, stream);
+}
+
+VGGT_API vggt_status vggt_frame_attn_qknorm(const void* q, const void* k, const void* v, void* o, vggt_dtype dt,
+                                            int S, int T, int H, const int32_t* pos_yx, float rope_base, float scale,
+                                            const vggt_qk_norm* norm, void* workspace, size_t ws_bytes,
+                                            void* stream) {
+  return frame_attn(q, k, v, o, dt, S, T, H, pos_yx, rope_base, scale, norm, workspace, ws_bytes, stream);
 }
 
 VGGT_API size_t vggt_global_attn_workspace(int S, int T, int H, int kv_splits, int rope_on, vggt_dtype dt) {
   if (!dtype_ok(dt) || !tokens_ok(S, T, H) || kv_splits < 0 || kv_splits > kMaxSplits) return 0;
   if (S == 0) return 0;
   const int64_t N = (int64_t)S * T;
-  return plan(1, N, N, H, T, rope_on != 0, true, kv_splits, dt).total;
+  return plan(1, N, N, H, T, (rope_on & VGGT_PRE_ROPE) != 0, true, kv_splits, dt, (rope_on & VGGT_PRE_QKNORM) != 0)
+      .total;
 }
 
 VGGT_API vggt_status vggt_global_attn(const void* q, const void* k, const void* v, void* o, vggt_dtype dt, int S,
                                       int T, int H, const int32_t* pos_yx, float rope_base, float scale,
                                       int kv_splits, void* workspace, size_t ws_bytes, void* stream) {
-  g_last_error[0] = 0;
-  if (!dtype_ok(dt)) return fail(VGGT_ERR_UNSUPPORTED, "unknown dtype %d", (int)dt);
-  if (!tokens_ok(S, T, H)) return fail(VGGT_ERR_SHAPE, "bad shape S=%d T=%d H=%d", S, T, H);
-  if (kv_splits < 0 || kv_splits > kMaxSplits) return fail(VGGT_ERR_SHAPE, "kv_splits must be in [0, %d]", kMaxSplits);
-  if (S == 0) return VGGT_OK;
-  const int64_t N = (int64_t)S * T;
-  const size_t bytes = (size_t)N * H * vggt::kHeadDim * elem_size(dt);
-  const Layout L = plan(1, N, N, H, T, pos_yx != nullptr, true, kv_splits, dt);
-  if (vggt_status s = validate_attn({q, k, v, o}, pos_yx, rope_base, L.total, workspace, ws_bytes, bytes, bytes))
-    return s;
-  if (vggt_status s = check_device()) return s;
-  hipError_t e = run_call(L, base_problem(q, k, v, o, H, scale), dt, 1, N, N, pos_yx, rope_base, T,
-                          (char*)workspace, (hipStream_t)stream, VGGT_TIMER_GLOBAL);
-  if (e != hipSuccess) return device_error("global attention launch", e);
-  return VGGT_OK;
+  return global_attn(q, k, v, o, dt, S, T, H, pos_yx, rope_base, scale, kv_splits, nullptr, workspace, ws_bytes,
+                     stream);
+}
+
+VGGT_API vggt_status vggt_global_attn_qknorm(const void* q, const void* k, const void* v, void* o, vggt_dtype dt,
+                                             int S, int T, int H, const int32_t* pos_yx, float rope_base, float scale,
+                                             int kv_splits, const vggt_qk_norm* norm, void* workspace,
+                                             size_t ws_bytes, void* stream) {
+  return global_attn(q, k, v, o, dt, S, T, H, pos_yx, rope_base, scale, kv_splits, norm, workspace, ws_bytes,
+                     stream);
 }
 
 // ---------------------------------------------------------------------------

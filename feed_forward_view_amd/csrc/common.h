@@ -58,6 +58,9 @@ struct AttnProblem {
   int splits;              // key ranges per sequence
   int keys_per_split;      // multiple of the key tile
   float scale_log2;        // softmax scale * log2(e)
+  const float* q_ln_g;     // bf16 kernel: per-head LayerNorm of Q before RoPE (gamma [64]), or null
+  const float* q_ln_b;     // beta [64]
+  float ln_eps;
 };
 
 // Launchers (stream-ordered, no synchronisation).  Return hipSuccess or the
@@ -69,7 +72,10 @@ hipError_t launch_rope(const void* src, void* dst, bool bf16, int64_t n_tok, int
                        double base, hipStream_t stream);
 hipError_t launch_rope_table(const int32_t* pos_yx, int T, double base, void* table, hipStream_t stream);
 hipError_t launch_k_tiles_bf16(const void* k, void* kt, int nseq, int len, int H, const void* table, int rope_T,
-                               hipStream_t stream);
+                               const float* ln_g, const float* ln_b, float ln_eps, hipStream_t stream);
+// Per-head LayerNorm of fp32 [n_tok][H][64] (src may equal dst).
+hipError_t launch_layer_norm_f32(const float* src, float* dst, int64_t n_tok, int H, const float* g, const float* b,
+                                 float eps, hipStream_t stream);
 hipError_t launch_v_tiles_bf16(const void* v, void* vt, int nseq, int len, int H, hipStream_t stream);
 // Append n keys (K and V [n][H][64] bf16) to single-sequence tile buffers that own
 // dst_ntile tiles per head, at key offset key0; keys of the last tile past key0 + n are

@@ -8,7 +8,8 @@
 //                     4/6, per axis; rope_base of the VGGT-Omega-1B-512-bf16
 //                     config article).
 //  k_tiles_kernel     K -> 64-key tiles in the attention kernel's LDS order,
-//                     rotated by the table when RoPE is on.
+//                     after an optional per-head LayerNorm and rotated by the
+//                     table when RoPE is on.
 //  v_tiles_kernel     V -> 64-key tiles of V^T in the attention kernel's LDS
 //                     order.
 // Each tile is 8 KiB and the attention kernel copies it linearly into LDS.
@@ -38,9 +39,14 @@ __device__ __forceinline__ int swz_vt(int d) { return (d ^ (d >> 3)) & 7; }
 // With a table, pairs are rotated as in rope_apply_kernel (the position of source key j
 // of sequence q is (q*len + j) % rope_T).  grid (tiles written, H, nseq); the first
 // tile written is key0 / 64 and each (sequence, head) owns dst_ntile tiles.
+//
+// With ln_g, every key's head vector is first centred and scaled by its per-head
+// LayerNorm (gamma ln_g, beta ln_b, eps ln_eps; the 8 lanes that hold one key row
+// reduce its 64 channels by xor shuffles), then rotated, then rounded once to bf16.
 __global__ __launch_bounds__(NT) void k_tiles_kernel(const uint16_t* __restrict__ k, u32x4* __restrict__ kt_out,
                                                      int len, int H, const f32x2* __restrict__ table, int rope_T,
-                                                     int key0, int dst_ntile) {
+                                                     int key0, int dst_ntile, const float* __restrict__ ln_g,
+                                                     const float* __restrict__ ln_b, float ln_eps) {
   const int tile = key0 / 64 + blockIdx.x, h = blockIdx.y, sq = blockIdx.z;
   u32x4* dst = kt_out + (((int64_t)sq * H + h) * dst_ntile + tile) * 512;
   const int64_t tok_stride = (int64_t)H * kHeadDim;
@@ -54,16 +60,46 @@ __global__ __launch_bounds__(NT) void k_tiles_kernel(const uint16_t* __restrict_
     u32x4 w = {0u, 0u, 0u, 0u};
     if (key < len) {
       w = *(const u32x4*)(k + ((int64_t)sq * len + key) * tok_stride + h * kHeadDim + 8 * u);
-      if (table) {
-        const int t = (int)(((int64_t)sq * len + key) % rope_T);
+      if (ln_g || table) {
+        float f[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const f32x2 cs = table[t * 32 + 4 * u + e];
-          if (cs[1] != 0.0f) {
-            const float x = lo_bf16(w[e]), y = hi_bf16(w[e]);
-            w[e] = pack_bf16x2(__builtin_fmaf(x, cs[0], -y * cs[1]), __builtin_fmaf(x, cs[1], y * cs[0]));
+          f[2 * e] = lo_bf16(w[e]);
+          f[2 * e + 1] = hi_bf16(w[e]);
+        }
+        if (ln_g) {
+          // the 8 lanes of this row hold its 8 units: sums over lanes xor 1, 2, 4
+          float sum = 0.0f;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) sum += f[j];
+          sum += __shfl_xor(sum, 1);
+          sum += __shfl_xor(sum, 2);
+          sum += __shfl_xor(sum, 4);
+          const float mu = sum * (1.0f / kHeadDim);
+          float dev = 0.0f;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) dev = __builtin_fmaf(f[j] - mu, f[j] - mu, dev);
+          dev += __shfl_xor(dev, 1);
+          dev += __shfl_xor(dev, 2);
+          dev += __shfl_xor(dev, 4);
+          const float inv = 1.0f / __builtin_sqrtf(dev * (1.0f / kHeadDim) + ln_eps);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) f[j] = __builtin_fmaf((f[j] - mu) * inv, ln_g[8 * u + j], ln_b[8 * u + j]);
+        }
+        if (table) {
+          const int t = (int)(((int64_t)sq * len + key) % rope_T);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const f32x2 cs = table[t * 32 + 4 * u + e];
+            if (cs[1] != 0.0f) {
+              const float x = f[2 * e], y = f[2 * e + 1];
+              f[2 * e] = __builtin_fmaf(x, cs[0], -y * cs[1]);
+              f[2 * e + 1] = __builtin_fmaf(x, cs[1], y * cs[0]);
+            }
           }
         }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(f[2 * e], f[2 * e + 1]);
       }
     }
     dst[i] = w;
@@ -129,11 +165,12 @@ hipError_t launch_rope_table(const int32_t* pos_yx, int T, double base, void* ta
 }
 
 hipError_t launch_k_tiles_bf16(const void* k, void* kt, int nseq, int len, int H, const void* table, int rope_T,
-                               hipStream_t stream) {
+                               const float* ln_g, const float* ln_b, float ln_eps, hipStream_t stream) {
   if (nseq <= 0 || len <= 0) return hipSuccess;
   const int ntile = (len + 63) / 64;
   hipLaunchKernelGGL(k_tiles_kernel, dim3((unsigned)ntile, (unsigned)H, (unsigned)nseq), dim3(NT), 0, stream,
-                     (const uint16_t*)k, (u32x4*)kt, len, H, (const f32x2*)table, rope_T, 0, ntile);
+                     (const uint16_t*)k, (u32x4*)kt, len, H, (const f32x2*)table, rope_T, 0, ntile, ln_g, ln_b,
+                     ln_eps);
   return hipGetLastError();
 }
 
@@ -150,7 +187,8 @@ hipError_t launch_tiles_append_bf16(const void* k, const void* v, void* kt, void
   if (n <= 0) return hipSuccess;
   const int tiles = (key0 + n - 1) / 64 - key0 / 64 + 1;
   hipLaunchKernelGGL(k_tiles_kernel, dim3((unsigned)tiles, (unsigned)H, 1u), dim3(NT), 0, stream,
-                     (const uint16_t*)k, (u32x4*)kt, n, H, (const f32x2*)nullptr, 1, key0, dst_ntile);
+                     (const uint16_t*)k, (u32x4*)kt, n, H, (const f32x2*)nullptr, 1, key0, dst_ntile,
+                     (const float*)nullptr, (const float*)nullptr, 0.0f);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(v_tiles_kernel, dim3((unsigned)tiles, (unsigned)H, 1u), dim3(NT), 0, stream,

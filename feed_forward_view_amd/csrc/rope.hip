@@ -84,7 +84,46 @@ __global__ __launch_bounds__(NT) void rope_kernel(const void* src, void* dst, in
   }
 }
 
+// Per-head LayerNorm of fp32 head vectors (the fp32 debug path's Q/K prologue):
+// one thread per (token, head) row of 64 channels, two passes over registers.
+__global__ __launch_bounds__(NT) void layer_norm_f32_kernel(const float* src, float* dst, int64_t rows,
+                                                            const float* __restrict__ g,
+                                                            const float* __restrict__ b, float eps) {
+  const int64_t r = (int64_t)blockIdx.x * NT + threadIdx.x;
+  if (r >= rows) return;
+  float f[D];
+#pragma unroll
+  for (int c = 0; c < D; c += 4) {
+    const f32x4 w = *(const f32x4*)(src + r * D + c);
+    f[c] = w[0]; f[c + 1] = w[1]; f[c + 2] = w[2]; f[c + 3] = w[3];
+  }
+  float sum = 0.0f;
+#pragma unroll
+  for (int c = 0; c < D; ++c) sum += f[c];
+  const float mu = sum * (1.0f / D);
+  float dev = 0.0f;
+#pragma unroll
+  for (int c = 0; c < D; ++c) dev = __builtin_fmaf(f[c] - mu, f[c] - mu, dev);
+  const float inv = 1.0f / __builtin_sqrtf(dev * (1.0f / D) + eps);
+#pragma unroll
+  for (int c = 0; c < D; c += 4) {
+    f32x4 w;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = __builtin_fmaf((f[c + j] - mu) * inv, g[c + j], b[c + j]);
+    *(f32x4*)(dst + r * D + c) = w;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_layer_norm_f32(const float* src, float* dst, int64_t n_tok, int H, const float* g, const float* b,
+                                 float eps, hipStream_t stream) {
+  const int64_t rows = n_tok * H;
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(layer_norm_f32_kernel, dim3((unsigned)((rows + NT - 1) / NT)), dim3(NT), 0, stream, src, dst,
+                     rows, g, b, eps);
+  return hipGetLastError();
+}
 
 hipError_t launch_rope(const void* src, void* dst, bool bf16, int64_t n_tok, int T, int H, const int32_t* pos_yx,
                        double base, hipStream_t stream) {

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define VGGT_ATTN_ABI_VERSION 2
+#define VGGT_ATTN_ABI_VERSION 3
 #define VGGT_HEAD_DIM 64
 
 typedef enum {
@@ -88,6 +88,31 @@ const char* vggt_last_error(void);
 vggt_status vggt_attn_rope(void* x, vggt_dtype dt, int S, int T, int H, const int32_t* pos_yx, float base,
                            void* stream);
 
+/* Flags of the workspace queries' `rope_on` argument: bit 0 = positions are
+ * passed (RoPE), bit 1 = a vggt_qk_norm is passed (Q/K LayerNorm).  Any other
+ * nonzero value than these bits reads as RoPE only, as before. */
+#define VGGT_PRE_ROPE 1
+#define VGGT_PRE_QKNORM 2
+
+/*
+ * Per-head LayerNorm of Q and K applied before RoPE (VGGT-JAX README,
+ * kernel-trial table: LayerNorm over the Q/K shapes, centred fp32 LayerNorm
+ * kept; VGGT-Omega-1B-512-bf16 config article: layer_norm_eps 1e-05).  For
+ * each token and head, over its 64 channels:
+ *   u' = (u - mean(u)) / sqrt(var(u) + eps) * gamma + beta   (biased variance)
+ * gamma/beta: [64] float32 device arrays shared by all heads; eps > 0.
+ * Computed in fp32 inside the K tile pre-pass and the attention kernel's Q
+ * prologue (fp32 debug mode: a separate pass into the rotated copies); the
+ * normalised and rotated values are rounded to bf16 once.
+ */
+typedef struct {
+  const float* q_gamma;
+  const float* q_beta;
+  const float* k_gamma;
+  const float* k_beta;
+  float eps;
+} vggt_qk_norm;
+
 /*
  * Frame-wise attention: S independent sequences of T tokens (slide deck
  * Section XI, slide 3/7; Section V, slide 5/10 for softmax(Q K^T / sqrt(d)) V,
@@ -104,6 +129,13 @@ size_t vggt_frame_attn_workspace(int S, int T, int H, int rope_on, vggt_dtype dt
 vggt_status vggt_frame_attn(const void* q, const void* k, const void* v, void* o, vggt_dtype dt, int S, int T,
                             int H, const int32_t* pos_yx, float rope_base, float scale, void* workspace,
                             size_t ws_bytes, void* stream);
+/* The same with the Q/K LayerNorm prologue (norm: host pointer, NULL = none;
+ * the workspace is sized with rope_on = VGGT_PRE_QKNORM | (RoPE ? VGGT_PRE_ROPE : 0)).
+ * VGGT_ERR_NULL if a parameter array is NULL, VGGT_ERR_SHAPE if eps <= 0,
+ * VGGT_ERR_ALIAS if a parameter array overlaps o or the workspace. */
+vggt_status vggt_frame_attn_qknorm(const void* q, const void* k, const void* v, void* o, vggt_dtype dt, int S, int T,
+                                   int H, const int32_t* pos_yx, float rope_base, float scale,
+                                   const vggt_qk_norm* norm, void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * Global attention over all N = S*T tokens (slide deck Section XI, slide 3/7;
@@ -117,6 +149,10 @@ size_t vggt_global_attn_workspace(int S, int T, int H, int kv_splits, int rope_o
 vggt_status vggt_global_attn(const void* q, const void* k, const void* v, void* o, vggt_dtype dt, int S, int T,
                              int H, const int32_t* pos_yx, float rope_base, float scale, int kv_splits,
                              void* workspace, size_t ws_bytes, void* stream);
+/* The same with the Q/K LayerNorm prologue, as for vggt_frame_attn_qknorm. */
+vggt_status vggt_global_attn_qknorm(const void* q, const void* k, const void* v, void* o, vggt_dtype dt, int S, int T,
+                                    int H, const int32_t* pos_yx, float rope_base, float scale, int kv_splits,
+                                    const vggt_qk_norm* norm, void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * FlashVGGT descriptor pooling (FlashVGGT README, "Overview": each frame's

@@ -32,7 +32,7 @@ def L():
 
 def test_exports_match_header(L):
     declared = header_functions()
-    assert len(declared) == 19
+    assert len(declared) == 21
     out = subprocess.run(["nm", "-D", "--defined-only", ffv.LIB_PATH], capture_output=True, text=True,
                          check=True).stdout
     exported = sorted(set(m for m in re.findall(r"\bT (vggt_\w+)", out)))
@@ -41,7 +41,7 @@ def test_exports_match_header(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.vggt_abi_version() == 2
+    assert L.vggt_abi_version() == 3
     for code, name in ffv.STATUS.items():
         assert L.vggt_status_str(code).decode() == name
     assert L.vggt_status_str(99).decode() == "VGGT_ERR_UNKNOWN"
@@ -177,3 +177,27 @@ def test_timer_arguments(L):
     assert n.value == -1
     assert L.vggt_timer_start(0) == SHAPE
     assert L.vggt_timer_start((1 << 20) + 1) == SHAPE
+
+
+def test_qk_norm_arguments(L):
+    BF16, F32 = 0, 1
+    S, T, H = 2, 40, 2
+    # the LayerNorm adds nothing to the bf16 workspace; fp32 keeps normalised copies of q and k
+    assert L.vggt_frame_attn_workspace(S, T, H, 2, BF16) == L.vggt_frame_attn_workspace(S, T, H, 0, BF16)
+    assert L.vggt_frame_attn_workspace(S, T, H, 2, F32) >= 2 * S * T * H * 64 * 4
+    assert L.vggt_global_attn_workspace(S, T, H, 1, 3, F32) == L.vggt_global_attn_workspace(S, T, H, 1, 1, F32)
+    G, Bt, KG, KB = 0x700000, 0x700100, 0x700200, 0x700300
+    norm = ffv.QkNorm(G, Bt, KG, KB, 1e-5)
+    f = L.vggt_frame_attn_qknorm
+    args = (_p(A), _p(B), _p(C), _p(O), 0, S, T, H, None, 100.0, 0.0)
+    bad = ffv.QkNorm(G, None, KG, KB, 1e-5)
+    assert f(*args, ctypes.byref(bad), None, 0, None) == NULL
+    bad = ffv.QkNorm(G, Bt, KG, KB, 0.0)
+    assert f(*args, ctypes.byref(bad), None, 0, None) == SHAPE
+    bad = ffv.QkNorm(G + 2, Bt, KG, KB, 1e-5)
+    assert f(*args, ctypes.byref(bad), None, 0, None) == ALIGN
+    bad = ffv.QkNorm(O + 64, Bt, KG, KB, 1e-5)  # gamma inside the output
+    assert f(*args, ctypes.byref(bad), _p(0x10000000), 1 << 24, None) == ALIAS
+    g = L.vggt_global_attn_qknorm
+    assert g(_p(A), _p(B), _p(C), _p(O), 0, S, T, H, None, 100.0, 0.0, 65, ctypes.byref(norm), None, 0,
+             None) == SHAPE
