@@ -214,3 +214,47 @@ def descriptor_stream_xattn(q, kd, vd, chunk_frames: int, scale=None, rows=None,
             out[sel] = attention(qf, kf[:f_end * Dn], vf[:f_end * Dn], scale=scale, rows=want[sel],
                                  nthreads=nthreads)
     return out
+
+
+def frame_attn_ex(q, k, v, S: int, T: int, T_active: int, pos=None, base: float = 100.0, scale=None,
+                  nthreads=None, q_norm=None, k_norm=None) -> np.ndarray:
+    """Frame attention over the first T_active tokens of each frame only
+    (VGGT-Omega-1B-512-bf16 config article, special-token notes: the 16
+    register tokens that follow each frame's patches join attention only in
+    some blocks).  q/k/v [S, T, H, D]; returns float64 [S, T_active, H, D]."""
+    H, D = q.shape[-2:]
+    sub = [to_f64(x).reshape(S, T, H, D)[:, :T_active] for x in (q, k, v)]
+    p = None if pos is None else np.asarray(pos).reshape(T, 2)[:T_active]
+    o = frame_attn(*sub, S, T_active, pos=p, base=base, scale=scale, nthreads=nthreads, q_norm=q_norm,
+                   k_norm=k_norm)
+    return o.reshape(S, T_active, H, D)
+
+
+def global_attn_ex(q, k, v, S: int, T: int, T_active: int, xq, xk, xv, pos=None, base: float = 100.0, scale=None,
+                   nthreads=None, q_norm=None, k_norm=None):
+    """Global attention over the first T_active tokens of every frame plus
+    n_extra sequence-level tokens (VGGT-Omega config article, special-token
+    notes: 4 storage tokens shared by all frames as global memory and one
+    camera token that gathers every frame's camera information).  The token
+    set is the active frame tokens in frame order followed by the extra
+    tokens; every token of the set is a query and a key.  Extra tokens carry
+    no position (identity rotation); the LayerNorm, if any, applies to all.
+    Returns (float64 [S, T_active, H, D], float64 [n_extra, H, D])."""
+    H, D = q.shape[-2:]
+    E = 0 if xq is None else int(np.asarray(xq).shape[0])
+
+    def tokens(x, xx):
+        a = to_f64(x).reshape(S, T, H, D)[:, :T_active].reshape(S * T_active, H, D)
+        return a if E == 0 else np.concatenate([a, to_f64(xx).reshape(E, H, D)])
+
+    qf, kf, vf = tokens(q, xq), tokens(k, xk), tokens(v, xv)
+    if q_norm is not None:
+        qf = layer_norm(qf, *q_norm)
+    if k_norm is not None:
+        kf = layer_norm(kf, *k_norm)
+    if pos is not None:
+        pt = np.concatenate([_frame_positions(np.asarray(pos).reshape(T, 2)[:T_active], S),
+                             np.zeros((E, 2), dtype=np.int32)])
+        qf, kf = rope(qf, pt, base), rope(kf, pt, base)
+    o = attention(qf, kf, vf, scale=scale, nthreads=nthreads)
+    return o[:S * T_active].reshape(S, T_active, H, D), o[S * T_active:]

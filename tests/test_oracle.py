@@ -361,6 +361,75 @@ def test_qk_norm_with_zero_gain_makes_keys_identical():
 
 
 # --------------------------------------------------------------------------
+# VGGT-Omega variants: register-free blocks and global-only extra tokens
+# --------------------------------------------------------------------------
+
+def _omega_tiny(seed, S=2, gh=3, gw=3, n_reg=2, E=3, H=2):
+    wl = workload.Workload("t", seed, S=S, gh=gh, gw=gw, n_special=n_reg, patch_begin=0, H=H, D=64)
+    q, k, v = (x.astype(np.float64) for x in wl.qkv_f32())
+    x = [workload.normal_f32(0xE0 + seed * 8 + i, (E, H, 64)).astype(np.float64) for i in range(3)]
+    return wl, q, k, v, x
+
+
+def test_global_ex_brute_force_with_registers_out_and_extras():
+    wl, q, k, v, (xq, xk, xv) = _omega_tiny(13)
+    S, T, Ta, H = wl.S, wl.T, wl.gh * wl.gw, wl.H
+    pos = wl.positions()
+    pt = np.concatenate([np.tile(pos[:Ta], (S, 1)), np.zeros((3, 2), dtype=np.int32)])
+    qs = np.concatenate([q[:, :Ta].reshape(-1, H, 64), xq])
+    ks = np.concatenate([k[:, :Ta].reshape(-1, H, 64), xk])
+    vs = np.concatenate([v[:, :Ta].reshape(-1, H, 64), xv])
+    ref = _einsum_attention(_einsum_rope(qs, pt, 100.0), _einsum_rope(ks, pt, 100.0), vs, 0.125)
+    of, ox = oracle.global_attn_ex(q, k, v, S, T, Ta, xq, xk, xv, pos=pos)
+    np.testing.assert_allclose(of.reshape(-1, H, 64), ref[:S * Ta], rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(ox, ref[S * Ta:], rtol=1e-11, atol=1e-13)
+    # register rows take no part: changing them changes nothing
+    k2, v2 = k.copy(), v.copy()
+    k2[:, Ta:] += 5.0
+    v2[:, Ta:] -= 2.0
+    of2, ox2 = oracle.global_attn_ex(q, k2, v2, S, T, Ta, xq, xk, xv, pos=pos)
+    np.testing.assert_array_equal(of2, of)
+    np.testing.assert_array_equal(ox2, ox)
+    # frame variant: the active tokens of each frame only
+    fe = oracle.frame_attn_ex(q, k, v, S, T, Ta, pos=pos)
+    pf = np.tile(pos[:Ta], (S, 1))
+    qr, kr = _einsum_rope(q[:, :Ta].reshape(-1, H, 64), pf, 100.0), _einsum_rope(k[:, :Ta].reshape(-1, H, 64), pf, 100.0)
+    vr = v[:, :Ta].reshape(-1, H, 64)
+    fref = np.concatenate([_einsum_attention(qr[s * Ta:(s + 1) * Ta], kr[s * Ta:(s + 1) * Ta], vr[s * Ta:(s + 1) * Ta],
+                                             0.125) for s in range(S)])
+    np.testing.assert_allclose(fe.reshape(-1, H, 64), fref, rtol=1e-11, atol=1e-13)
+
+
+def test_global_ex_reduces_to_global_attention():
+    wl, q, k, v, _ = _omega_tiny(14)
+    pos = wl.positions()
+    of, ox = oracle.global_attn_ex(q, k, v, wl.S, wl.T, wl.T, None, None, None, pos=pos)
+    assert ox.shape[0] == 0
+    np.testing.assert_array_equal(of.reshape(wl.N, wl.H, 64), oracle.global_attn(q, k, v, wl.S, wl.T, pos=pos))
+
+
+def test_global_ex_extra_tokens_are_keys_and_queries_of_everything():
+    wl, q, k, v, (xq, xk, xv) = _omega_tiny(15, H=1)
+    S, T, Ta = wl.S, wl.T, wl.gh * wl.gw
+    # a dominant extra key: every query selects that extra token's value
+    xk2 = xk.copy()
+    xk2[1] = 0.0
+    qpos = np.abs(q).max() + 1.0
+    q2 = np.zeros_like(q) + qpos
+    xq2 = np.zeros_like(xq) + qpos
+    xk2[1, :, :] = 40.0
+    of, ox = oracle.global_attn_ex(q2, k, v, S, T, Ta, xq2, xk2, xv)
+    np.testing.assert_allclose(of, np.broadcast_to(xv[1], of.shape), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(ox, np.broadcast_to(xv[1], ox.shape), rtol=0, atol=1e-12)
+    # identical keys: each output is the mean of the values of all active and extra tokens
+    zk, zx = np.zeros_like(k), np.zeros_like(xk)
+    of, ox = oracle.global_attn_ex(q, zk, v, S, T, Ta, xq, zx, xv)
+    mean = np.concatenate([v[:, :Ta].reshape(-1, 1, 64), xv]).mean(axis=0)
+    np.testing.assert_allclose(of, np.broadcast_to(mean, of.shape), rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(ox, np.broadcast_to(mean, ox.shape), rtol=1e-13, atol=1e-15)
+
+
+# --------------------------------------------------------------------------
 # Descriptor pooling and cross-attention
 # --------------------------------------------------------------------------
 
