@@ -70,6 +70,7 @@ def main() -> int:
     ap.add_argument("--workload", default="vggt-518-s32")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stream", action="store_true", help="skip the FlashVGGT chunk-recursive measurement")
+    ap.add_argument("--no-omega", action="store_true", help="skip the VGGT-Omega 64-frame measurement")
     ap.add_argument("--cpu-row-stride", type=int, default=48)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (hardware-counter calibration)")
@@ -222,6 +223,9 @@ def main() -> int:
     result["qknorm"] = bench_qknorm(ffv, qd, kd, vd, posd, go, fo, ws_g, ws_f, max(3, args.steps // 2), flops)
     if not args.no_stream:
         result["stream"] = bench_stream(ffv, dev, max(3, args.steps // 2), 2)
+    if not args.no_omega:
+        del qd, kd, vd, fo, go, xo, kpool, vpool, ws_f, ws_g, ws_x
+        result["omega"] = bench_omega(ffv, dev, max(3, args.steps // 4))
     if not args.no_cpu_baseline:
         result["cpu_baseline"], result["parity_sample"] = cpu_baseline(wl, q, k, v, pos, Dn, ph, pw, go, fo, xo,
                                                                        args.cpu_row_stride)
@@ -266,6 +270,60 @@ def bench_qknorm(ffv, qd, kd, vd, posd, go, fo, ws_g, ws_f, iters, flops):
         out[f"{kind}_kernel_ms"] = round(float(np.mean(kern)), 4)
         out[f"{kind}_call_tflops"] = round(flops[kind] / (call_ms * 1e-3) / 1e12, 2)
     return out
+
+
+def bench_omega(ffv, dev, iters):
+    """VGGT-Omega, 64 frames of 32x32 patches + 16 registers (N = 66560): global
+    attention with the registers in, and the register-free form with the 4
+    storage + 1 camera extra tokens (65536 + 5 tokens)."""
+    import torch
+
+    import workload
+
+    wl = workload.WORKLOADS["omega-512-s64"]
+    S, T, H = wl.S, wl.T, wl.H
+    Ta, E = wl.gh * wl.gw, 5
+    q, k, v = wl.qkv_bf16()
+
+    def to_dev(a):
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    del q, k, v
+    x = [to_dev(workload.normal_bf16(0x0E6A5 + i, (E, H, 64))) for i in range(3)]
+    pd = torch.from_numpy(wl.positions()).to(dev)
+    out = torch.empty_like(qd)
+    xo = torch.empty_like(x[0])
+    ws_g = torch.empty(max(1, ffv.vggt_global_attn_workspace(S, T, H, 0, True)), dtype=torch.uint8, device=dev)
+    ws_e = torch.empty(max(1, int(ffv.lib().vggt_global_attn_ex_workspace(S, T, Ta, E, H, 0, ffv.PRE_ROPE, 0))),
+                       dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    calls = {
+        "global": lambda: ffv.vggt_global_attn(qd, kd, vd, out=out, pos_yx=pd, workspace=ws_g),
+        "global_ex": lambda: ffv.vggt_global_attn_ex(qd, kd, vd, Ta, *x, out=out, xout=xo, pos_yx=pd,
+                                                     workspace=ws_e),
+    }
+    flops = {"global": attn_flops(S * T, S * T, H), "global_ex": attn_flops(S * Ta + E, S * Ta + E, H)}
+    res = {"workload": f"{wl.name}: S={S} frames x T={T} (32x32 patches + 16 registers), H={H}, d=64, RoPE base "
+                       f"100; global_ex = {Ta} patch tokens per frame + {E} extra tokens"}
+    for name, fn in calls.items():
+        fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+        torch.cuda.synchronize()
+        ffv.vggt_timer_start(2 * iters)
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        kern = [ms for _, ms in ffv.vggt_timer_stop()]
+        call_ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+        kernel_ms = float(np.sum(kern)) / iters  # global_ex: frame-token and extra-token launches
+        res[f"{name}_call_ms"] = round(call_ms, 4)
+        res[f"{name}_kernel_ms"] = round(kernel_ms, 4)
+        res[f"{name}_kernel_tflops"] = round(flops[name] / (kernel_ms * 1e-3) / 1e12, 2)
+        res[f"{name}_kernel_frac_of_bf16_peak"] = round(flops[name] / (kernel_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+    return res
 
 
 def bench_stream(ffv, dev, passes, warmup, chunk_frames=10):

@@ -57,6 +57,11 @@ SIGNATURES = {
     "vggt_descriptor_cache_attn_workspace": (_sz, [_i, _i, _i, _i, _i]),
     "vggt_descriptor_cache_attn": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]),
     "vggt_descriptor_chunked_xattn": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp]),
+    "vggt_frame_attn_ex_workspace": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "vggt_frame_attn_ex": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _f, _f, _np, _vp, _sz, _vp]),
+    "vggt_global_attn_ex_workspace": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i]),
+    "vggt_global_attn_ex": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _vp, _f, _f, _i,
+                                 _np, _vp, _sz, _vp]),
     "vggt_timer_start": (_i, [_i]),
     "vggt_timer_stop": (_i, [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(_i), _i, ctypes.POINTER(_i)]),
 }
@@ -245,6 +250,53 @@ def vggt_global_attn_qknorm(q, k, v, q_norm, k_norm, eps=1e-5, out=None, pos_yx=
                                          _pos(pos_yx, T), rope_base, scale, kv_splits, ctypes.byref(norm), _ptr(ws),
                                          nbytes, _stream(stream)))
     return out
+
+
+def _norm_arg(q_norm, k_norm, eps, H):
+    if q_norm is None and k_norm is None:
+        return None, 0
+    if q_norm is None or k_norm is None:
+        raise ValueError("give both q_norm and k_norm, or neither")
+    return ctypes.byref(_qk_norm(q_norm, k_norm, eps, H)), PRE_QKNORM
+
+
+def vggt_frame_attn_ex(q, k, v, T_active, out=None, pos_yx=None, rope_base=100.0, scale=0.0, q_norm=None,
+                       k_norm=None, eps=1e-5, workspace=None, stream=None):
+    """Frame attention over the first T_active tokens of each frame of [S, T, H, 64];
+    rows past T_active of `out` are left as they are (allocated empty when out is None)."""
+    S, T, H, out = _check_qkv(q, k, v, out)
+    norm, flags = _norm_arg(q_norm, k_norm, eps, H)
+    flags |= PRE_ROPE if pos_yx is not None else 0
+    need = int(lib().vggt_frame_attn_ex_workspace(S, T, T_active, H, flags, _dtype_code(q)))
+    ws, nbytes = _workspace(need, q.device, workspace)
+    _check("vggt_frame_attn_ex",
+           lib().vggt_frame_attn_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _dtype_code(q), S, T, T_active, H,
+                                    _pos(pos_yx, T), rope_base, scale, norm, _ptr(ws), nbytes, _stream(stream)))
+    return out
+
+
+def vggt_global_attn_ex(q, k, v, T_active, xq=None, xk=None, xv=None, out=None, xout=None, pos_yx=None,
+                        rope_base=100.0, scale=0.0, kv_splits=0, q_norm=None, k_norm=None, eps=1e-5,
+                        workspace=None, stream=None):
+    """Global attention over the first T_active tokens of every frame plus the extra
+    tokens xq/xk/xv [E, H, 64]; returns (out, xout)."""
+    S, T, H, out = _check_qkv(q, k, v, out)
+    E = 0 if xq is None else int(xq.shape[0])
+    if E:
+        for n, t in (("xq", xq), ("xk", xk), ("xv", xv)):
+            if t is None or tuple(t.shape) != (E, H, HEAD_DIM) or t.dtype != q.dtype or not t.is_contiguous():
+                raise ValueError(f"{n} must be a contiguous [{E}, {H}, 64] tensor of q's dtype")
+        xout = torch.empty_like(xq) if xout is None else xout
+    norm, flags = _norm_arg(q_norm, k_norm, eps, H)
+    flags |= PRE_ROPE if pos_yx is not None else 0
+    need = int(lib().vggt_global_attn_ex_workspace(S, T, T_active, E, H, kv_splits, flags, _dtype_code(q)))
+    ws, nbytes = _workspace(need, q.device, workspace)
+    _check("vggt_global_attn_ex",
+           lib().vggt_global_attn_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _dtype_code(q), S, T, T_active, H,
+                                     _ptr(xq if E else None), _ptr(xk if E else None), _ptr(xv if E else None),
+                                     _ptr(xout if E else None), E, _pos(pos_yx, T), rope_base, scale, kv_splits,
+                                     norm, _ptr(ws), nbytes, _stream(stream)))
+    return out, (xout if E else None)
 
 
 def vggt_descriptor_count(T, gh, gw, ph, pw) -> int:

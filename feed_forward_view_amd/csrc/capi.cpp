@@ -318,9 +318,10 @@ hipError_t run_call(const Layout& L, vggt::AttnProblem p, vggt_dtype dt, int nse
       p.rope_tab = (const vggt::f32x2*)table;
       p.rope_T = rope_T;
     }
-    e = vggt::launch_k_tiles_bf16(p.k, ws + L.kt, nseq, (int)nk, H, table, rope_T, norm ? norm->k_gamma : nullptr,
-                                  norm ? norm->k_beta : nullptr, norm ? norm->eps : 0.0f, st);
-    if (e == hipSuccess) e = vggt::launch_v_tiles_bf16(p.v, ws + L.vt, nseq, (int)nk, H, st);
+    e = vggt::launch_k_tiles_bf16(vggt::contiguous_keys(p.k, (int)nk), ws + L.kt, nseq, (int)nk, H, table, rope_T,
+                                  norm ? norm->k_gamma : nullptr, norm ? norm->k_beta : nullptr,
+                                  norm ? norm->eps : 0.0f, st);
+    if (e == hipSuccess) e = vggt::launch_v_tiles_bf16(vggt::contiguous_keys(p.v, (int)nk), ws + L.vt, nseq, (int)nk, H, st);
     if (e != hipSuccess) return e;
     p.k = ws + L.kt;
     p.vt = ws + L.vt;
@@ -758,4 +759,279 @@ VGGT_API vggt_status vggt_timer_stop(float* ms, int* kinds, int n_max, int* n_re
   if (n_recorded) *n_recorded = n;
   timer_release_locked();
   return st;
+}
+
+// ---------------------------------------------------------------------------
+// VGGT-Omega block variants: a subset of each frame's tokens, and global-only
+// extra tokens
+// ---------------------------------------------------------------------------
+
+namespace {
+
+constexpr int kMaxExtra = 4096;
+
+// Workspace of one frame/global "ex" call.  bf16: RoPE table and the key
+// tiles of the compacted key set; fp32: normalised/rotated copies and the
+// gathered key set.  Global calls also hold the split partials of the frame
+// tokens' queries and of the extra tokens' queries.
+struct ExLayout {
+  size_t table = 0, kt = 0, vt = 0, qr = 0, kc = 0, vc = 0, xqr = 0;
+  size_t part_o = 0, part_ml = 0, xpart_o = 0, xpart_ml = 0, total = 0;
+  bool use_qr = false, use_kc = false, use_vc = false, use_xqr = false;
+  int nseq_k = 1;
+  int64_t nk = 0;
+  int ktiles = 0;
+  SplitPlan sp{1, 0}, spx{1, 0};
+};
+
+void add_ex(ExLayout& L, size_t& off, size_t bytes) {
+  off = L.total;
+  L.total += align256(bytes);
+}
+
+ExLayout plan_ex(bool global, int S, int T, int Ta, int E, int H, int kv_splits, bool rope, bool norm,
+                 vggt_dtype dt) {
+  ExLayout L;
+  const size_t row = (size_t)H * vggt::kHeadDim * elem_size(dt);
+  L.nseq_k = global ? 1 : S;
+  L.nk = global ? (int64_t)S * Ta + E : Ta;
+  if (dt == VGGT_BF16) {
+    if (rope) add_ex(L, L.table, (size_t)T * 32 * 8);
+    L.ktiles = (int)((L.nk + 63) / 64);
+    const size_t tiles = (size_t)L.nseq_k * H * L.ktiles * 64 * vggt::kHeadDim * 2;
+    add_ex(L, L.kt, tiles);
+    add_ex(L, L.vt, tiles);
+  } else {
+    if (rope || norm) {
+      L.use_qr = true;
+      add_ex(L, L.qr, (size_t)S * T * row);
+    }
+    if (global) {
+      L.use_kc = L.use_vc = true;
+      add_ex(L, L.kc, (size_t)L.nk * row);
+      add_ex(L, L.vc, (size_t)L.nk * row);
+    } else if (rope || norm) {
+      L.use_kc = true;
+      add_ex(L, L.kc, (size_t)S * T * row);
+    }
+    if (global && norm && E > 0) {
+      L.use_xqr = true;
+      add_ex(L, L.xqr, (size_t)E * row);
+    }
+  }
+  if (global) {
+    const int bq = query_tile(dt);
+    // workgroups see S sequences of ceil(Ta / bq) query tiles
+    L.sp = plan_splits((int64_t)S * ((Ta + bq - 1) / bq) * bq, L.nk, H, kv_splits, dt);
+    if (L.sp.splits > 1) {
+      add_ex(L, L.part_o, (size_t)L.sp.splits * S * Ta * H * vggt::kHeadDim * 4);
+      add_ex(L, L.part_ml, (size_t)L.sp.splits * S * Ta * H * 2 * 4);
+    }
+    if (E > 0) {
+      L.spx = plan_splits(E, L.nk, H, 0, dt);
+      if (L.spx.splits > 1) {
+        add_ex(L, L.xpart_o, (size_t)L.spx.splits * E * H * vggt::kHeadDim * 4);
+        add_ex(L, L.xpart_ml, (size_t)L.spx.splits * E * H * 2 * 4);
+      }
+    }
+  } else {
+    L.sp = SplitPlan{1, (int)pad64(Ta)};
+  }
+  return L;
+}
+
+struct ExArgs {
+  bool global;
+  const void *q, *k, *v;
+  void* o;
+  const void *xq, *xk, *xv;
+  void* xo;
+  int S, T, Ta, E, H;
+  const int32_t* pos;
+  float base, scale;
+  const vggt_qk_norm* norm;
+};
+
+hipError_t run_ex(const ExLayout& L, const ExArgs& a, vggt_dtype dt, char* ws, hipStream_t st) {
+  hipError_t e = hipSuccess;
+  const int H = a.H;
+  vggt::AttnProblem p = base_problem(a.q, a.k, a.v, a.o, H, a.scale);
+  vggt::KeySrc ks, vs;
+  ks.main = a.k;
+  vs.main = a.v;
+  if (a.global) {
+    ks.extra = a.xk;
+    vs.extra = a.xv;
+    ks.frame_len = vs.frame_len = a.Ta;
+    ks.frame_stride = vs.frame_stride = a.T;
+    ks.n_main = vs.n_main = (int64_t)a.S * a.Ta;
+  } else {
+    ks.seq_rows = vs.seq_rows = a.T;
+    ks.n_main = vs.n_main = a.Ta;
+  }
+  if (dt == VGGT_BF16) {
+    const void* table = nullptr;
+    if (a.pos) {
+      e = vggt::launch_rope_table(a.pos, a.T, (double)a.base, ws + L.table, st);
+      if (e != hipSuccess) return e;
+      table = ws + L.table;
+      p.rope_tab = (const vggt::f32x2*)table;
+      p.rope_T = a.T;
+    }
+    if (a.norm) {
+      p.q_ln_g = a.norm->q_gamma;
+      p.q_ln_b = a.norm->q_beta;
+      p.ln_eps = a.norm->eps;
+    }
+    e = vggt::launch_k_tiles_bf16(ks, ws + L.kt, L.nseq_k, (int)L.nk, H, table, a.T,
+                                  a.norm ? a.norm->k_gamma : nullptr, a.norm ? a.norm->k_beta : nullptr,
+                                  a.norm ? a.norm->eps : 0.0f, st);
+    if (e == hipSuccess) e = vggt::launch_v_tiles_bf16(vs, ws + L.vt, L.nseq_k, (int)L.nk, H, st);
+    if (e != hipSuccess) return e;
+    p.k = ws + L.kt;
+    p.vt = ws + L.vt;
+    p.ktiles_seq = L.ktiles;
+  } else {
+    const int64_t full = (int64_t)a.S * a.T;
+    if (L.use_qr) {
+      const void* src = a.q;
+      if (a.norm) {
+        e = vggt::launch_layer_norm_f32((const float*)a.q, (float*)(ws + L.qr), full, H, a.norm->q_gamma,
+                                        a.norm->q_beta, a.norm->eps, st);
+        src = ws + L.qr;
+      }
+      if (e == hipSuccess && a.pos) e = vggt::launch_rope(src, ws + L.qr, false, full, a.T, H, a.pos, (double)a.base, st);
+      if (e != hipSuccess) return e;
+      p.q = ws + L.qr;
+    }
+    if (a.global) {
+      // the compacted key set: active frame tokens in frame order, then the extras
+      e = vggt::launch_gather_keys_f32(ks, (float*)(ws + L.kc), 1, (int)L.nk, H, st);
+      if (e == hipSuccess) e = vggt::launch_gather_keys_f32(vs, (float*)(ws + L.vc), 1, (int)L.nk, H, st);
+      if (e == hipSuccess && a.norm)
+        e = vggt::launch_layer_norm_f32((const float*)(ws + L.kc), (float*)(ws + L.kc), L.nk, H, a.norm->k_gamma,
+                                        a.norm->k_beta, a.norm->eps, st);
+      if (e == hipSuccess && a.pos)
+        e = vggt::launch_rope(ws + L.kc, ws + L.kc, false, (int64_t)a.S * a.Ta, a.Ta, H, a.pos, (double)a.base, st);
+      if (e != hipSuccess) return e;
+      p.k = ws + L.kc;
+      p.v = ws + L.vc;
+    } else if (L.use_kc) {
+      const void* src = a.k;
+      if (a.norm) {
+        e = vggt::launch_layer_norm_f32((const float*)a.k, (float*)(ws + L.kc), full, H, a.norm->k_gamma,
+                                        a.norm->k_beta, a.norm->eps, st);
+        src = ws + L.kc;
+      }
+      if (e == hipSuccess && a.pos) e = vggt::launch_rope(src, ws + L.kc, false, full, a.T, H, a.pos, (double)a.base, st);
+      if (e != hipSuccess) return e;
+      p.k = ws + L.kc;
+    }
+  }
+  // the frame tokens' queries: S sequences of Ta rows, T rows apart
+  p.nseq = a.S;
+  p.nq = a.Ta;
+  p.q_seq_stride = a.T;
+  p.nq_total = (int64_t)a.S * a.Ta;
+  p.nk = (int)L.nk;
+  p.k_seq_stride = a.global ? 0 : (dt == VGGT_BF16 ? L.nk : a.T);
+  p.splits = L.sp.splits;
+  p.keys_per_split = L.sp.keys_per_split;
+  if (L.sp.splits > 1) {
+    p.part_o = (float*)(ws + L.part_o);
+    p.part_ml = (float*)(ws + L.part_ml);
+  }
+  e = run_attention(p, dt, st, a.global ? VGGT_TIMER_GLOBAL : VGGT_TIMER_FRAME);
+  if (e != hipSuccess || !a.global || a.E == 0) return e;
+  // the extra tokens' queries: one sequence of E rows against the same keys, no rotation
+  vggt::AttnProblem x = p;
+  x.q = (dt == VGGT_F32 && L.use_xqr) ? (const void*)(ws + L.xqr) : a.xq;
+  if (dt == VGGT_F32 && L.use_xqr) {
+    e = vggt::launch_layer_norm_f32((const float*)a.xq, (float*)(ws + L.xqr), a.E, H, a.norm->q_gamma,
+                                    a.norm->q_beta, a.norm->eps, st);
+    if (e != hipSuccess) return e;
+  }
+  x.o = a.xo;
+  x.rope_tab = nullptr;
+  x.nseq = 1;
+  x.nq = a.E;
+  x.q_seq_stride = 0;
+  x.nq_total = a.E;
+  x.splits = L.spx.splits;
+  x.keys_per_split = L.spx.keys_per_split;
+  x.part_o = L.spx.splits > 1 ? (float*)(ws + L.xpart_o) : nullptr;
+  x.part_ml = L.spx.splits > 1 ? (float*)(ws + L.xpart_ml) : nullptr;
+  return run_attention(x, dt, st, VGGT_TIMER_GLOBAL);
+}
+
+vggt_status ex_call(const ExArgs& a, vggt_dtype dt, int kv_splits, void* workspace, size_t ws_bytes, void* stream) {
+  g_last_error[0] = 0;
+  if (!dtype_ok(dt)) return fail(VGGT_ERR_UNSUPPORTED, "unknown dtype %d", (int)dt);
+  if (!tokens_ok(a.S, a.T, a.H) || a.Ta < 1 || a.Ta > a.T || a.E < 0 || a.E > kMaxExtra ||
+      (!a.global && a.E != 0))
+    return fail(VGGT_ERR_SHAPE, "bad shape S=%d T=%d T_active=%d n_extra=%d H=%d", a.S, a.T, a.Ta, a.E, a.H);
+  if (kv_splits < 0 || kv_splits > kMaxSplits) return fail(VGGT_ERR_SHAPE, "kv_splits must be in [0, %d]", kMaxSplits);
+  if (vggt_status s = check_norm(a.norm)) return s;
+  if (a.S == 0) return VGGT_OK;
+  const size_t bytes = (size_t)a.S * a.T * a.H * vggt::kHeadDim * elem_size(dt);
+  const size_t xbytes = (size_t)a.E * a.H * vggt::kHeadDim * elem_size(dt);
+  const ExLayout L = plan_ex(a.global, a.S, a.T, a.Ta, a.E, a.H, kv_splits, a.pos != nullptr, a.norm != nullptr, dt);
+  if (vggt_status s = validate_attn({a.q, a.k, a.v, a.o}, a.pos, a.base, L.total, workspace, ws_bytes, bytes, bytes))
+    return s;
+  if (vggt_status s = check_norm_alias(a.norm, a.o, bytes, workspace, L.total)) return s;
+  if (a.E > 0) {
+    if (!a.xq || !a.xk || !a.xv || !a.xo) return fail(VGGT_ERR_NULL, "xq, xk, xv and xo are required");
+    if (!aligned16(a.xq) || !aligned16(a.xk) || !aligned16(a.xv) || !aligned16(a.xo))
+      return fail(VGGT_ERR_ALIGN, "extra-token tensors must be 16-byte aligned");
+    for (const void* in : {a.q, a.k, a.v})
+      if (overlap(a.xo, xbytes, in, bytes)) return fail(VGGT_ERR_ALIAS, "xo overlaps q, k or v");
+    for (const void* in : {a.xq, a.xk, a.xv})
+      if (overlap(a.xo, xbytes, in, xbytes) || overlap(a.o, bytes, in, xbytes))
+        return fail(VGGT_ERR_ALIAS, "an output overlaps an extra-token input");
+    if (overlap(a.xo, xbytes, a.o, bytes) || overlap(a.xo, xbytes, workspace, L.total))
+      return fail(VGGT_ERR_ALIAS, "xo overlaps o or the workspace");
+    if (vggt_status s = check_norm_alias(a.norm, a.xo, xbytes, nullptr, 0)) return s;
+  }
+  if (vggt_status s = check_device()) return s;
+  hipError_t e = run_ex(L, a, dt, (char*)workspace, (hipStream_t)stream);
+  if (e != hipSuccess) return device_error(a.global ? "global attention (ex) launch" : "frame attention (ex) launch", e);
+  return VGGT_OK;
+}
+
+}  // namespace
+
+VGGT_API size_t vggt_frame_attn_ex_workspace(int S, int T, int T_active, int H, int flags, vggt_dtype dt) {
+  if (!dtype_ok(dt) || !tokens_ok(S, T, H) || T_active < 1 || T_active > T) return 0;
+  if (S == 0) return 0;
+  return plan_ex(false, S, T, T_active, 0, H, 1, (flags & VGGT_PRE_ROPE) != 0, (flags & VGGT_PRE_QKNORM) != 0, dt)
+      .total;
+}
+
+VGGT_API vggt_status vggt_frame_attn_ex(const void* q, const void* k, const void* v, void* o, vggt_dtype dt, int S,
+                                        int T, int T_active, int H, const int32_t* pos_yx, float rope_base,
+                                        float scale, const vggt_qk_norm* norm, void* workspace, size_t ws_bytes,
+                                        void* stream) {
+  const ExArgs a{false, q, k, v, o, nullptr, nullptr, nullptr, nullptr, S, T, T_active, 0, H, pos_yx, rope_base,
+                 scale, norm};
+  return ex_call(a, dt, 1, workspace, ws_bytes, stream);
+}
+
+VGGT_API size_t vggt_global_attn_ex_workspace(int S, int T, int T_active, int n_extra, int H, int kv_splits,
+                                              int flags, vggt_dtype dt) {
+  if (!dtype_ok(dt) || !tokens_ok(S, T, H) || T_active < 1 || T_active > T || n_extra < 0 ||
+      n_extra > kMaxExtra || kv_splits < 0 || kv_splits > kMaxSplits)
+    return 0;
+  if (S == 0) return 0;
+  return plan_ex(true, S, T, T_active, n_extra, H, kv_splits, (flags & VGGT_PRE_ROPE) != 0,
+                 (flags & VGGT_PRE_QKNORM) != 0, dt)
+      .total;
+}
+
+VGGT_API vggt_status vggt_global_attn_ex(const void* q, const void* k, const void* v, void* o, vggt_dtype dt, int S,
+                                         int T, int T_active, int H, const void* xq, const void* xk, const void* xv,
+                                         void* xo, int n_extra, const int32_t* pos_yx, float rope_base, float scale,
+                                         int kv_splits, const vggt_qk_norm* norm, void* workspace, size_t ws_bytes,
+                                         void* stream) {
+  const ExArgs a{true, q, k, v, o, xq, xk, xv, xo, S, T, T_active, n_extra, H, pos_yx, rope_base, scale, norm};
+  return ex_call(a, dt, kv_splits, workspace, ws_bytes, stream);
 }

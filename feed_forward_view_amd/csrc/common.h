@@ -71,12 +71,36 @@ hipError_t launch_attn_merge(const AttnProblem& p, bool out_bf16, hipStream_t st
 hipError_t launch_rope(const void* src, void* dst, bool bf16, int64_t n_tok, int T, int H, const int32_t* pos_yx,
                        double base, hipStream_t stream);
 hipError_t launch_rope_table(const int32_t* pos_yx, int T, double base, void* table, hipStream_t stream);
-hipError_t launch_k_tiles_bf16(const void* k, void* kt, int nseq, int len, int H, const void* table, int rope_T,
+// Where key j (0 <= j < len) of sequence s lives: keys [0, n_main) are rows of
+// `main` -- row s*seq_rows + j, or, with frame_len > 0, row s*seq_rows +
+// (j / frame_len) * frame_stride + j % frame_len -- and keys [n_main, len) are
+// rows j - n_main of `extra`.  Rows are [H][64] elements.
+struct KeySrc {
+  const void* main = nullptr;
+  const void* extra = nullptr;
+  int64_t seq_rows = 0;
+  int frame_len = 0;
+  int64_t frame_stride = 0;
+  int64_t n_main = 0;
+};
+inline KeySrc contiguous_keys(const void* k, int len) {
+  KeySrc s;
+  s.main = k;
+  s.seq_rows = len;
+  s.n_main = len;
+  return s;
+}
+
+// K -> tiles for nseq sequences of len keys (RoPE position of a main row r is
+// r % rope_T; extra rows are not rotated), with an optional per-head LayerNorm.
+hipError_t launch_k_tiles_bf16(const KeySrc& k, void* kt, int nseq, int len, int H, const void* table, int rope_T,
                                const float* ln_g, const float* ln_b, float ln_eps, hipStream_t stream);
 // Per-head LayerNorm of fp32 [n_tok][H][64] (src may equal dst).
 hipError_t launch_layer_norm_f32(const float* src, float* dst, int64_t n_tok, int H, const float* g, const float* b,
                                  float eps, hipStream_t stream);
-hipError_t launch_v_tiles_bf16(const void* v, void* vt, int nseq, int len, int H, hipStream_t stream);
+hipError_t launch_v_tiles_bf16(const KeySrc& v, void* vt, int nseq, int len, int H, hipStream_t stream);
+// fp32 rows of a key source gathered into a contiguous [nseq*len][H][64] copy.
+hipError_t launch_gather_keys_f32(const KeySrc& src, float* dst, int nseq, int len, int H, hipStream_t stream);
 // Append n keys (K and V [n][H][64] bf16) to single-sequence tile buffers that own
 // dst_ntile tiles per head, at key offset key0; keys of the last tile past key0 + n are
 // zeroed, keys below key0 are kept.

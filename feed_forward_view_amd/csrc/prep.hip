@@ -29,21 +29,34 @@ __global__ __launch_bounds__(NT) void rope_table_kernel(const int32_t* __restric
   table[i] = f32x2{(float)cos(theta), (float)sin(theta)};
 }
 
+// Row of key j of sequence sq in src.main (>= 0), or -1 - (row in src.extra).
+__device__ __forceinline__ int64_t key_row(const KeySrc& src, int sq, int64_t j) {
+  if (j >= src.n_main) return -1 - (j - src.n_main);
+  const int64_t r = src.frame_len > 0 ? (j / src.frame_len) * src.frame_stride + j % src.frame_len : j;
+  return (int64_t)sq * src.seq_rows + r;
+}
+
+template <typename T>
+__device__ __forceinline__ const T* key_ptr(const KeySrc& src, int64_t row, int64_t row_elems) {
+  return row >= 0 ? (const T*)src.main + row * row_elems : (const T*)src.extra + (-1 - row) * row_elems;
+}
+
 __device__ __forceinline__ int rho_key(int i) { return (i & ~0xC) | ((i & 4) << 1) | ((i & 8) >> 1); }
 __device__ __forceinline__ int swz_vt(int d) { return (d ^ (d >> 3)) & 7; }
 
-// K [nseq*len][H][64] -> KT [nseq][H][ntile][64 rows][8 slots of 16 bytes]: row r of tile
+// K (key j of sequence q at the row given by the KeySrc) -> KT [nseq][H][ntile][64 rows]
+// [8 slots of 16 bytes]: row r of tile
 // kt holds key 64*kt + rho(r), slot s holds its channels 8u..8u+7 with u = s ^ (r & 7).
 // Source key j lands on tile key key0 + j; tile keys below key0 keep what the buffer
 // holds (appending to a filled prefix), tile keys at or past key0 + len become zero.
-// With a table, pairs are rotated as in rope_apply_kernel (the position of source key j
-// of sequence q is (q*len + j) % rope_T).  grid (tiles written, H, nseq); the first
+// With a table, pairs are rotated as in rope_apply_kernel (the position of a key on main
+// row r is r % rope_T; extra keys are not rotated).  grid (tiles written, H, nseq); the first
 // tile written is key0 / 64 and each (sequence, head) owns dst_ntile tiles.
 //
 // With ln_g, every key's head vector is first centred and scaled by its per-head
 // LayerNorm (gamma ln_g, beta ln_b, eps ln_eps; the 8 lanes that hold one key row
 // reduce its 64 channels by xor shuffles), then rotated, then rounded once to bf16.
-__global__ __launch_bounds__(NT) void k_tiles_kernel(const uint16_t* __restrict__ k, u32x4* __restrict__ kt_out,
+__global__ __launch_bounds__(NT) void k_tiles_kernel(KeySrc k, u32x4* __restrict__ kt_out,
                                                      int len, int H, const f32x2* __restrict__ table, int rope_T,
                                                      int key0, int dst_ntile, const float* __restrict__ ln_g,
                                                      const float* __restrict__ ln_b, float ln_eps) {
@@ -59,8 +72,9 @@ __global__ __launch_bounds__(NT) void k_tiles_kernel(const uint16_t* __restrict_
     const int u = slot ^ (r & 7);
     u32x4 w = {0u, 0u, 0u, 0u};
     if (key < len) {
-      w = *(const u32x4*)(k + ((int64_t)sq * len + key) * tok_stride + h * kHeadDim + 8 * u);
-      if (ln_g || table) {
+      const int64_t row = key_row(k, sq, key);
+      w = *(const u32x4*)(key_ptr<uint16_t>(k, row, tok_stride) + h * kHeadDim + 8 * u);
+      if (ln_g || (table && row >= 0)) {
         float f[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -86,8 +100,8 @@ __global__ __launch_bounds__(NT) void k_tiles_kernel(const uint16_t* __restrict_
 #pragma unroll
           for (int j = 0; j < 8; ++j) f[j] = __builtin_fmaf((f[j] - mu) * inv, ln_g[8 * u + j], ln_b[8 * u + j]);
         }
-        if (table) {
-          const int t = (int)(((int64_t)sq * len + key) % rope_T);
+        if (table && row >= 0) {
+          const int t = (int)(row % rope_T);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const f32x2 cs = table[t * 32 + 4 * u + e];
@@ -106,13 +120,13 @@ __global__ __launch_bounds__(NT) void k_tiles_kernel(const uint16_t* __restrict_
   }
 }
 
-// V [nseq*len][H][64] -> VT [nseq][H][ntile][64 channel rows][8 slots]: slot s of row d
+// V (rows as for k_tiles_kernel) -> VT [nseq][H][ntile][64 channel rows][8 slots]: slot s of row d
 // holds tile keys 8u .. 8u+7 of channel d, u = s ^ swz_vt(d).  Source key j lands on tile
 // key key0 + j; tile keys below key0 keep their contents (a slot that straddles key0 is
 // merged with what the buffer holds), tile keys at or past key0 + len become zero.
 // grid (tiles written, H, nseq) as for k_tiles_kernel; the 64 x 64 tile is transposed
 // through LDS.
-__global__ __launch_bounds__(NT) void v_tiles_kernel(const uint16_t* __restrict__ v, u32x4* __restrict__ vt_out,
+__global__ __launch_bounds__(NT) void v_tiles_kernel(KeySrc v, u32x4* __restrict__ vt_out,
                                                      int len, int H, int key0, int dst_ntile) {
   __shared__ uint32_t tile_s[64][33];  // [key][channel pair], padded
   const int tile = key0 / 64 + blockIdx.x, h = blockIdx.y, sq = blockIdx.z;
@@ -124,7 +138,8 @@ __global__ __launch_bounds__(NT) void v_tiles_kernel(const uint16_t* __restrict_
     const int j = i >> 3, u = i & 7;  // tile key, unit of 8 channels
     const int key = kfirst + j;
     u32x4 w = {0u, 0u, 0u, 0u};
-    if (key >= 0 && key < len) w = *(const u32x4*)(v + ((int64_t)sq * len + key) * tok_stride + h * kHeadDim + 8 * u);
+    if (key >= 0 && key < len)
+      w = *(const u32x4*)(key_ptr<uint16_t>(v, key_row(v, sq, key), tok_stride) + h * kHeadDim + 8 * u);
 #pragma unroll
     for (int e = 0; e < 4; ++e) tile_s[j][4 * u + e] = w[e];
   }
@@ -156,6 +171,20 @@ __global__ __launch_bounds__(NT) void v_tiles_kernel(const uint16_t* __restrict_
   }
 }
 
+// fp32 key rows -> contiguous copy [nseq*len][H][64]; one thread per 16-byte unit.
+__global__ __launch_bounds__(NT) void gather_keys_f32_kernel(KeySrc src, float* __restrict__ dst, int len, int H,
+                                                             int64_t units) {
+  const int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x;
+  if (i >= units) return;
+  const int64_t row_units = (int64_t)H * 16;
+  const int64_t key = i / row_units;  // over nseq*len
+  const int64_t within = i % row_units;
+  const int sq = (int)(key / len);
+  const int64_t row = key_row(src, sq, key % len);
+  const f32x4 w = *(const f32x4*)(key_ptr<float>(src, row, (int64_t)H * kHeadDim) + 4 * within);
+  *(f32x4*)(dst + 4 * i) = w;
+}
+
 }  // namespace
 
 hipError_t launch_rope_table(const int32_t* pos_yx, int T, double base, void* table, hipStream_t stream) {
@@ -164,21 +193,28 @@ hipError_t launch_rope_table(const int32_t* pos_yx, int T, double base, void* ta
   return hipGetLastError();
 }
 
-hipError_t launch_k_tiles_bf16(const void* k, void* kt, int nseq, int len, int H, const void* table, int rope_T,
+hipError_t launch_k_tiles_bf16(const KeySrc& k, void* kt, int nseq, int len, int H, const void* table, int rope_T,
                                const float* ln_g, const float* ln_b, float ln_eps, hipStream_t stream) {
   if (nseq <= 0 || len <= 0) return hipSuccess;
   const int ntile = (len + 63) / 64;
-  hipLaunchKernelGGL(k_tiles_kernel, dim3((unsigned)ntile, (unsigned)H, (unsigned)nseq), dim3(NT), 0, stream,
-                     (const uint16_t*)k, (u32x4*)kt, len, H, (const f32x2*)table, rope_T, 0, ntile, ln_g, ln_b,
-                     ln_eps);
+  hipLaunchKernelGGL(k_tiles_kernel, dim3((unsigned)ntile, (unsigned)H, (unsigned)nseq), dim3(NT), 0, stream, k,
+                     (u32x4*)kt, len, H, (const f32x2*)table, rope_T, 0, ntile, ln_g, ln_b, ln_eps);
   return hipGetLastError();
 }
 
-hipError_t launch_v_tiles_bf16(const void* v, void* vt, int nseq, int len, int H, hipStream_t stream) {
+hipError_t launch_v_tiles_bf16(const KeySrc& v, void* vt, int nseq, int len, int H, hipStream_t stream) {
   if (nseq <= 0 || len <= 0) return hipSuccess;
   const int ntile = (len + 63) / 64;
-  hipLaunchKernelGGL(v_tiles_kernel, dim3((unsigned)ntile, (unsigned)H, (unsigned)nseq), dim3(NT), 0, stream,
-                     (const uint16_t*)v, (u32x4*)vt, len, H, 0, ntile);
+  hipLaunchKernelGGL(v_tiles_kernel, dim3((unsigned)ntile, (unsigned)H, (unsigned)nseq), dim3(NT), 0, stream, v,
+                     (u32x4*)vt, len, H, 0, ntile);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_keys_f32(const KeySrc& src, float* dst, int nseq, int len, int H, hipStream_t stream) {
+  const int64_t units = (int64_t)nseq * len * H * 16;  // 16-byte units
+  if (units <= 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_keys_f32_kernel, dim3((unsigned)((units + NT - 1) / NT)), dim3(NT), 0, stream, src, dst,
+                     len, H, units);
   return hipGetLastError();
 }
 
@@ -187,12 +223,12 @@ hipError_t launch_tiles_append_bf16(const void* k, const void* v, void* kt, void
   if (n <= 0) return hipSuccess;
   const int tiles = (key0 + n - 1) / 64 - key0 / 64 + 1;
   hipLaunchKernelGGL(k_tiles_kernel, dim3((unsigned)tiles, (unsigned)H, 1u), dim3(NT), 0, stream,
-                     (const uint16_t*)k, (u32x4*)kt, n, H, (const f32x2*)nullptr, 1, key0, dst_ntile,
+                     contiguous_keys(k, n), (u32x4*)kt, n, H, (const f32x2*)nullptr, 1, key0, dst_ntile,
                      (const float*)nullptr, (const float*)nullptr, 0.0f);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(v_tiles_kernel, dim3((unsigned)tiles, (unsigned)H, 1u), dim3(NT), 0, stream,
-                     (const uint16_t*)v, (u32x4*)vt, n, H, key0, dst_ntile);
+                     contiguous_keys(v, n), (u32x4*)vt, n, H, key0, dst_ntile);
   return hipGetLastError();
 }
 

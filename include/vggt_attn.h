@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define VGGT_ATTN_ABI_VERSION 3
+#define VGGT_ATTN_ABI_VERSION 4
 #define VGGT_HEAD_DIM 64
 
 typedef enum {
@@ -153,6 +153,44 @@ vggt_status vggt_global_attn(const void* q, const void* k, const void* v, void* 
 vggt_status vggt_global_attn_qknorm(const void* q, const void* k, const void* v, void* o, vggt_dtype dt, int S, int T,
                                     int H, const int32_t* pos_yx, float rope_base, float scale, int kv_splits,
                                     const vggt_qk_norm* norm, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * VGGT-Omega block variants (VGGT-Omega-1B-512-bf16 config article, field
+ * table and special-token notes: 16 register tokens follow each frame's
+ * patches and join attention only in blocks 2, 6, 9, 14 and 20; 4 storage
+ * tokens are shared by all frames as global memory; one camera token gathers
+ * the camera information of every frame).
+ *
+ * Tokens keep the [S, T, H, 64] layout; only the first T_active tokens of each
+ * frame take part (1 <= T_active <= T; T_active = T - 16 in the blocks without
+ * registers).  Rows T_active..T-1 of every frame of o are left untouched.
+ *
+ * vggt_frame_attn_ex: each frame's active tokens attend to that frame's
+ * active tokens.
+ *
+ * vggt_global_attn_ex: the token set is every frame's active tokens, in frame
+ * order, followed by n_extra sequence-level tokens (xq, xk, xv, xo
+ * [n_extra, H, 64], dtype dt; NULL allowed when n_extra == 0).  Every token of
+ * the set is a query and a key.  Extra tokens carry no position (identity
+ * rotation); the LayerNorm, if given, applies to them too.  kv_splits applies
+ * to the frame tokens' queries; the extra tokens' queries (a separate launch
+ * over the same prepared keys) always use the library's split choice.
+ * n_extra in [0, 4096].  No output may overlap an input (VGGT_ERR_ALIAS).
+ *
+ * Positions, scale, norm (NULL = none) and the workspace are as for
+ * vggt_frame_attn_qknorm; `flags` of the workspace queries are
+ * VGGT_PRE_ROPE | VGGT_PRE_QKNORM as used by the call.
+ */
+size_t vggt_frame_attn_ex_workspace(int S, int T, int T_active, int H, int flags, vggt_dtype dt);
+vggt_status vggt_frame_attn_ex(const void* q, const void* k, const void* v, void* o, vggt_dtype dt, int S, int T,
+                               int T_active, int H, const int32_t* pos_yx, float rope_base, float scale,
+                               const vggt_qk_norm* norm, void* workspace, size_t ws_bytes, void* stream);
+size_t vggt_global_attn_ex_workspace(int S, int T, int T_active, int n_extra, int H, int kv_splits, int flags,
+                                     vggt_dtype dt);
+vggt_status vggt_global_attn_ex(const void* q, const void* k, const void* v, void* o, vggt_dtype dt, int S, int T,
+                                int T_active, int H, const void* xq, const void* xk, const void* xv, void* xo,
+                                int n_extra, const int32_t* pos_yx, float rope_base, float scale, int kv_splits,
+                                const vggt_qk_norm* norm, void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * FlashVGGT descriptor pooling (FlashVGGT README, "Overview": each frame's

@@ -231,7 +231,7 @@ def frame_attn_ex(q, k, v, S: int, T: int, T_active: int, pos=None, base: float 
 
 
 def global_attn_ex(q, k, v, S: int, T: int, T_active: int, xq, xk, xv, pos=None, base: float = 100.0, scale=None,
-                   nthreads=None, q_norm=None, k_norm=None):
+                   nthreads=None, q_norm=None, k_norm=None, rows=None):
     """Global attention over the first T_active tokens of every frame plus
     n_extra sequence-level tokens (VGGT-Omega config article, special-token
     notes: 4 storage tokens shared by all frames as global memory and one
@@ -239,7 +239,9 @@ def global_attn_ex(q, k, v, S: int, T: int, T_active: int, xq, xk, xv, pos=None,
     set is the active frame tokens in frame order followed by the extra
     tokens; every token of the set is a query and a key.  Extra tokens carry
     no position (identity rotation); the LayerNorm, if any, applies to all.
-    Returns (float64 [S, T_active, H, D], float64 [n_extra, H, D])."""
+    Returns (float64 [S, T_active, H, D], float64 [n_extra, H, D]); with rows
+    (indices into the set: frame tokens first, then the extras) it returns
+    float64 [len(rows), H, D] instead."""
     H, D = q.shape[-2:]
     E = 0 if xq is None else int(np.asarray(xq).shape[0])
 
@@ -256,5 +258,7 @@ def global_attn_ex(q, k, v, S: int, T: int, T_active: int, xq, xk, xv, pos=None,
         pt = np.concatenate([_frame_positions(np.asarray(pos).reshape(T, 2)[:T_active], S),
                              np.zeros((E, 2), dtype=np.int32)])
         qf, kf = rope(qf, pt, base), rope(kf, pt, base)
+    if rows is not None:
+        return attention(qf, kf, vf, scale=scale, rows=rows, nthreads=nthreads)
     o = attention(qf, kf, vf, scale=scale, nthreads=nthreads)
     return o[:S * T_active].reshape(S, T_active, H, D), o[S * T_active:]

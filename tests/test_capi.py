@@ -32,7 +32,7 @@ def L():
 
 def test_exports_match_header(L):
     declared = header_functions()
-    assert len(declared) == 21
+    assert len(declared) == 25
     out = subprocess.run(["nm", "-D", "--defined-only", ffv.LIB_PATH], capture_output=True, text=True,
                          check=True).stdout
     exported = sorted(set(m for m in re.findall(r"\bT (vggt_\w+)", out)))
@@ -41,7 +41,7 @@ def test_exports_match_header(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.vggt_abi_version() == 3
+    assert L.vggt_abi_version() == 4
     for code, name in ffv.STATUS.items():
         assert L.vggt_status_str(code).decode() == name
     assert L.vggt_status_str(99).decode() == "VGGT_ERR_UNKNOWN"
@@ -201,3 +201,30 @@ def test_qk_norm_arguments(L):
     g = L.vggt_global_attn_qknorm
     assert g(_p(A), _p(B), _p(C), _p(O), 0, S, T, H, None, 100.0, 0.0, 65, ctypes.byref(norm), None, 0,
              None) == SHAPE
+
+
+def test_omega_variant_arguments(L):
+    BF16, F32 = 0, 1
+    S, T, Ta, E, H = 4, 1040, 1024, 5, 16
+    # bf16: tiles of the compacted key set (frame: per frame; global: active tokens plus extras)
+    assert L.vggt_frame_attn_ex_workspace(S, T, Ta, H, 0, BF16) == 2 * S * H * 16 * 64 * 64 * 2
+    ws = L.vggt_global_attn_ex_workspace(S, T, Ta, E, H, 1, 0, BF16)
+    assert ws >= 2 * H * ((S * Ta + E + 63) // 64) * 64 * 64 * 2
+    assert L.vggt_global_attn_ex_workspace(S, T, T + 1, E, H, 1, 0, BF16) == 0
+    assert L.vggt_global_attn_ex_workspace(S, T, Ta, 4097, H, 1, 0, BF16) == 0
+    # fp32 global always gathers the key set
+    assert L.vggt_global_attn_ex_workspace(S, T, Ta, E, H, 1, 0, F32) >= 2 * (S * Ta + E) * H * 64 * 4
+    g = L.vggt_global_attn_ex
+    X, XK, XV, XO = 0x800000, 0x810000, 0x820000, 0x830000
+    # (q, k, v, o, dt, S, T, T_active, H, xq, xk, xv, xo, n_extra, pos, base, scale, kv_splits, norm, ws, ws_bytes, st)
+    assert g(_p(A), _p(B), _p(C), _p(O), 0, 2, 8, 9, 1, None, None, None, None, 0, None, 100.0, 0.0, 0, None,
+             None, 0, None) == SHAPE  # T_active > T
+    assert g(_p(A), _p(B), _p(C), _p(O), 0, 2, 8, 6, 1, _p(X), None, _p(XV), _p(XO), 2, None, 100.0, 0.0, 0, None,
+             _p(0x10000000), 1 << 24, None) == NULL
+    assert g(_p(A), _p(B), _p(C), _p(O), 0, 2, 8, 6, 1, _p(X), _p(XK), _p(XV), _p(A), 2, None, 100.0, 0.0, 0,
+             None, _p(0x10000000), 1 << 24, None) == ALIAS  # xo is q
+    assert g(_p(A), _p(B), _p(C), _p(O), 0, 2, 8, 6, 1, _p(X + 8), _p(XK), _p(XV), _p(XO), 2, None, 100.0, 0.0, 0,
+             None, _p(0x10000000), 1 << 24, None) == ALIGN
+    f = L.vggt_frame_attn_ex
+    assert f(_p(A), _p(B), _p(C), _p(O), 0, 2, 8, 0, 1, None, 100.0, 0.0, None, None, 0, None) == SHAPE
+    assert f(_p(A), _p(B), _p(C), _p(O), 0, 2, 8, 6, 1, None, 100.0, 0.0, None, None, 0, None) == WS

@@ -383,6 +383,9 @@ def test_global_ex_brute_force_with_registers_out_and_extras():
     of, ox = oracle.global_attn_ex(q, k, v, S, T, Ta, xq, xk, xv, pos=pos)
     np.testing.assert_allclose(of.reshape(-1, H, 64), ref[:S * Ta], rtol=1e-11, atol=1e-13)
     np.testing.assert_allclose(ox, ref[S * Ta:], rtol=1e-11, atol=1e-13)
+    rows = np.array([0, Ta, S * Ta - 1, S * Ta, S * Ta + 2])
+    np.testing.assert_array_equal(oracle.global_attn_ex(q, k, v, S, T, Ta, xq, xk, xv, pos=pos, rows=rows),
+                                  np.concatenate([of.reshape(-1, H, 64), ox])[rows])
     # register rows take no part: changing them changes nothing
     k2, v2 = k.copy(), v.copy()
     k2[:, Ta:] += 5.0
