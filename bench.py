@@ -38,9 +38,9 @@ PEAK_HBM_GBS = 8000.0
 # plain 1 GiB copy (profiles/attn_fwd_bf16_vggt-518-s32_counters.md).  Valid
 # only for the kernel source it was measured on.
 PROFILED_TRAFFIC = {
-    "kernel_source_sha256": "9655204c72958de885d8684a77f30a2ae2089d162a58540c65e421097c295cc5",
-    "read_bytes": 1381.5e6,
-    "write_bytes": 416.5e6,
+    "kernel_source_sha256": "c07bfc7c40dbf28d614702e5894d5367bf48343502341ef15c6a036df2f5c86e",
+    "read_bytes": 1330.7e6,
+    "write_bytes": 405.2e6,
 }
 
 
@@ -71,6 +71,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stream", action="store_true", help="skip the FlashVGGT chunk-recursive measurement")
     ap.add_argument("--no-omega", action="store_true", help="skip the VGGT-Omega 64-frame measurement")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time only the headline step (no Q/K-norm, streaming or Omega sections)")
     ap.add_argument("--cpu-row-stride", type=int, default=48)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (hardware-counter calibration)")
@@ -220,11 +222,11 @@ def main() -> int:
         "input_gen_s": round(gen_s, 2),
     }
 
-    result["qknorm"] = bench_qknorm(ffv, qd, kd, vd, posd, go, fo, ws_g, ws_f, max(3, args.steps // 2), flops)
-    if not args.no_stream:
+    if not args.no_extras:
+        result["qknorm"] = bench_qknorm(ffv, qd, kd, vd, posd, ws_g, ws_f, max(3, args.steps // 2), flops)
+    if not (args.no_stream or args.no_extras):
         result["stream"] = bench_stream(ffv, dev, max(3, args.steps // 2), 2)
-    if not args.no_omega:
-        del qd, kd, vd, fo, go, xo, kpool, vpool, ws_f, ws_g, ws_x
+    if not (args.no_omega or args.no_extras):
         result["omega"] = bench_omega(ffv, dev, max(3, args.steps // 4))
     if not args.no_cpu_baseline:
         result["cpu_baseline"], result["parity_sample"] = cpu_baseline(wl, q, k, v, pos, Dn, ph, pw, go, fo, xo,
@@ -233,14 +235,16 @@ def main() -> int:
     return 0
 
 
-def bench_qknorm(ffv, qd, kd, vd, posd, go, fo, ws_g, ws_f, iters, flops):
+def bench_qknorm(ffv, qd, kd, vd, posd, ws_g, ws_f, iters, flops):
     """Frame and global attention of the same workload with the fused per-head
-    Q/K LayerNorm + RoPE prologue (seeded gamma/beta around (1, 0))."""
+    Q/K LayerNorm + RoPE prologue (seeded gamma/beta around (1, 0)), into
+    outputs of their own."""
     import torch
 
     import workload
 
     dev = qd.device
+    fo, go = torch.empty_like(qd), torch.empty_like(qd)
     prm = [torch.from_numpy(workload.normal_f32(0x1A7E + i, (64,)) * 0.3 + (1.0 if i % 2 == 0 else 0.0)).to(dev)
            for i in range(4)]
     qn, kn = (prm[0], prm[1]), (prm[2], prm[3])
