@@ -50,6 +50,10 @@ def lib():
         L.oracle_attention.restype = ctypes.c_int
         L.oracle_layer_norm.argtypes = [dp, ctypes.c_int64, ctypes.c_int, ctypes.c_int, dp, dp, ctypes.c_double]
         L.oracle_layer_norm.restype = None
+        L.oracle_attention_backward.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, ctypes.c_int64, ctypes.c_int64,
+                                                ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                                ctypes.c_double, lp, ctypes.c_int64, lp, ctypes.c_int64, ctypes.c_int]
+        L.oracle_attention_backward.restype = ctypes.c_int
         L.oracle_descriptor_count.argtypes = [ctypes.c_int] * 5
         L.oracle_descriptor_count.restype = ctypes.c_int
         L.oracle_descriptor_pool.argtypes = [dp, dp] + [ctypes.c_int] * 9
@@ -262,3 +266,68 @@ def global_attn_ex(q, k, v, S: int, T: int, T_active: int, xq, xk, xv, pos=None,
         return attention(qf, kf, vf, scale=scale, rows=rows, nthreads=nthreads)
     o = attention(qf, kf, vf, scale=scale, nthreads=nthreads)
     return o[:S * T_active].reshape(S, T_active, H, D), o[S * T_active:]
+
+
+def _idx(a):
+    if a is None:
+        return None, 0, None
+    r = np.ascontiguousarray(a, dtype=np.int64).reshape(-1)
+    return r, r.size, r.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+
+
+def attention_backward(q, k, v, dout, *, group_q: int = 0, group_k: int = 0, scale=None, rows=None, cols=None,
+                       nthreads=None):
+    """Gradients of multi-head attention (oracle.c, oracle_attention_backward).
+    q/dout [nq, H, D], k/v [nk, H, D].  Returns (dq [len(rows) or nq, H, D],
+    dk, dv [len(cols) or nk, H, D], lse [nq, H]) in float64; lse is the natural
+    log-normaliser of every query row."""
+    q64, k64, v64, d64 = (np.ascontiguousarray(to_f64(x), dtype=np.float64) for x in (q, k, v, dout))
+    nq, H, D = q64.shape
+    nk = k64.shape[0]
+    assert k64.shape == v64.shape == (nk, H, D) and d64.shape == (nq, H, D)
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    r, nr, rp = _idx(rows)
+    c, nc, cp = _idx(cols)
+    dq = np.zeros((nr if r is not None else nq, H, D))
+    dk = np.zeros((nc if c is not None else nk, H, D))
+    dv = np.zeros_like(dk)
+    lse = np.zeros((nq, H))
+    rc = lib().oracle_attention_backward(_dp(q64), _dp(k64), _dp(v64), _dp(d64), _dp(dq), _dp(dk), _dp(dv),
+                                         _dp(lse), nq, nk, H, D, group_q, group_k, float(scale), rp, nr, cp, nc,
+                                         nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_attention_backward: bad arguments")
+    return dq, dk, dv, lse
+
+
+def _attn_backward(q, k, v, dout, S, T, pos, base, scale, rows, cols, nthreads, frame):
+    """RoPE-aware gradients: the attention runs on q' = R q and k' = R k (R a
+    rotation per position), so dq = R^T dq' and dk = R^T dk', and R^T is the
+    rotation by the negated position."""
+    H, D = q.shape[-2:]
+    qf, kf, vf, df = (to_f64(x).reshape(S * T, H, D) for x in (q, k, v, dout))
+    if pos is not None:
+        pt = _frame_positions(pos, S)
+        qf, kf = rope(qf, pt, base), rope(kf, pt, base)
+    g = T if frame else 0
+    dq, dk, dv, lse = attention_backward(qf, kf, vf, df, group_q=g, group_k=g, scale=scale, rows=rows, cols=cols,
+                                         nthreads=nthreads)
+    if pos is not None:
+        pt = _frame_positions(pos, S)
+        back = -pt
+        dq = rope(dq, back if rows is None else back[np.asarray(rows)], base)
+        dk = rope(dk, back if cols is None else back[np.asarray(cols)], base)
+    return dq, dk, dv, lse
+
+
+def frame_attn_backward(q, k, v, dout, S: int, T: int, pos=None, base: float = 100.0, scale=None, rows=None,
+                        cols=None, nthreads=None):
+    """Gradients of frame_attn: (dq, dk, dv, lse); rows/cols index the [S*T] token axis."""
+    return _attn_backward(q, k, v, dout, S, T, pos, base, scale, rows, cols, nthreads, True)
+
+
+def global_attn_backward(q, k, v, dout, S: int, T: int, pos=None, base: float = 100.0, scale=None, rows=None,
+                         cols=None, nthreads=None):
+    """Gradients of global_attn: (dq, dk, dv, lse); rows/cols index the [S*T] token axis."""
+    return _attn_backward(q, k, v, dout, S, T, pos, base, scale, rows, cols, nthreads, False)

@@ -241,6 +241,173 @@ int oracle_attention(const double* q, const double* k, const double* v, double* 
 }
 
 /* ------------------------------------------------------------------------ */
+/* Attention gradients                                                      */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * The chain rule through one head of o_i = sum_j p_ij v_j,
+ * p_ij = exp(s_ij) / sum_l exp(s_il), s_ij = scale <q_i, k_j>, given the
+ * upstream gradient do_i of every output row:
+ *   dv_j  = sum_i p_ij do_i
+ *   dp_ij = <do_i, v_j>
+ *   ds_ij = p_ij (dp_ij - sum_l p_il dp_il)      (Jacobian of the softmax row)
+ *   dq_i  = scale sum_j ds_ij k_j
+ *   dk_j  = scale sum_i ds_ij q_i
+ * lse_i = log sum_l exp(s_il) is the row's log-normaliser, so that
+ * p_ij = exp(s_ij - lse_i).  Key sets (group_q/group_k) as for
+ * oracle_attention.  The work is done in three plain passes per head:
+ *   1. every query row: lse_i and c_i = sum_l p_il dp_il (two-pass softmax);
+ *   2. the requested query rows: dq_i;
+ *   3. the requested key rows: dk_j and dv_j, summing over the queries whose
+ *      key set holds j.
+ * rows/cols select query/key tokens (NULL = all); dq is [nrows][H][D], dk and
+ * dv are [ncols][H][D].  Threads split (head, row) items of each pass.
+ */
+typedef struct {
+  const double *q, *k, *v, *dout;
+  double *dq, *dk, *dv, *lse, *csum;
+  int64_t nq, nk;
+  int H, D;
+  int64_t group_q, group_k;
+  double scale;
+  const int64_t *rows, *cols;
+  int64_t nrows, ncols;
+  int phase;
+  int64_t next;
+  pthread_mutex_t lock;
+} bwd_job;
+
+static void key_range(const bwd_job* J, int64_t i, int64_t* k0, int64_t* nk) {
+  *k0 = 0;
+  *nk = J->nk;
+  if (J->group_q > 0) {
+    *k0 = (i / J->group_q) * J->group_k;
+    *nk = J->group_k;
+  }
+}
+
+static double dot(const double* a, const double* b, int D) {
+  double s = 0.0;
+  for (int d = 0; d < D; ++d) s += a[d] * b[d];
+  return s;
+}
+
+static void* bwd_worker(void* arg) {
+  bwd_job* J = (bwd_job*)arg;
+  const int64_t stride = (int64_t)J->H * J->D;
+  const int D = J->D;
+  const int64_t kmax = J->group_q > 0 ? J->group_k : J->nk;
+  double* sc = (double*)malloc(sizeof(double) * (size_t)(kmax > 0 ? kmax : 1));
+  const int64_t items = J->phase == 1 ? J->nq : (J->phase == 2 ? J->nrows : J->ncols);
+  for (;;) {
+    pthread_mutex_lock(&J->lock);
+    const int64_t item = J->next;
+    J->next += 1;
+    pthread_mutex_unlock(&J->lock);
+    if (item >= items * J->H) break;
+    const int64_t it = item / J->H;
+    const int h = (int)(item % J->H);
+    if (J->phase == 1 || J->phase == 2) {
+      const int64_t i = J->phase == 1 ? it : (J->rows ? J->rows[it] : it);
+      int64_t k0, nk;
+      key_range(J, i, &k0, &nk);
+      const double* qi = J->q + i * stride + (int64_t)h * D;
+      const double* doi = J->dout + i * stride + (int64_t)h * D;
+      if (J->phase == 1) {
+        double m = -INFINITY;
+        for (int64_t j = 0; j < nk; ++j) {
+          sc[j] = J->scale * dot(qi, J->k + (k0 + j) * stride + (int64_t)h * D, D);
+          if (sc[j] > m) m = sc[j];
+        }
+        double l = 0.0;
+        for (int64_t j = 0; j < nk; ++j) l += exp(sc[j] - m);
+        const double lse = m + log(l);
+        double c = 0.0;
+        for (int64_t j = 0; j < nk; ++j)
+          c += exp(sc[j] - lse) * dot(doi, J->v + (k0 + j) * stride + (int64_t)h * D, D);
+        J->lse[i * J->H + h] = lse;
+        J->csum[i * J->H + h] = c;
+      } else {
+        double* dqi = J->dq + it * stride + (int64_t)h * D;
+        for (int d = 0; d < D; ++d) dqi[d] = 0.0;
+        const double lse = J->lse[i * J->H + h], c = J->csum[i * J->H + h];
+        for (int64_t j = 0; j < nk; ++j) {
+          const double* kj = J->k + (k0 + j) * stride + (int64_t)h * D;
+          const double p = exp(J->scale * dot(qi, kj, D) - lse);
+          const double ds = p * (dot(doi, J->v + (k0 + j) * stride + (int64_t)h * D, D) - c);
+          for (int d = 0; d < D; ++d) dqi[d] += J->scale * ds * kj[d];
+        }
+      }
+    } else {
+      const int64_t j = J->cols ? J->cols[it] : it;
+      const double* kj = J->k + j * stride + (int64_t)h * D;
+      const double* vj = J->v + j * stride + (int64_t)h * D;
+      double* dkj = J->dk + it * stride + (int64_t)h * D;
+      double* dvj = J->dv + it * stride + (int64_t)h * D;
+      for (int d = 0; d < D; ++d) dkj[d] = dvj[d] = 0.0;
+      int64_t i0 = 0, i1 = J->nq;  /* queries whose key set holds key j */
+      if (J->group_q > 0) {
+        i0 = (j / J->group_k) * J->group_q;
+        i1 = i0 + J->group_q;
+      }
+      for (int64_t i = i0; i < i1; ++i) {
+        const double* qi = J->q + i * stride + (int64_t)h * D;
+        const double* doi = J->dout + i * stride + (int64_t)h * D;
+        const double p = exp(J->scale * dot(qi, kj, D) - J->lse[i * J->H + h]);
+        const double ds = p * (dot(doi, vj, D) - J->csum[i * J->H + h]);
+        for (int d = 0; d < D; ++d) {
+          dvj[d] += p * doi[d];
+          dkj[d] += J->scale * ds * qi[d];
+        }
+      }
+    }
+  }
+  free(sc);
+  return NULL;
+}
+
+int oracle_attention_backward(const double* q, const double* k, const double* v, const double* dout, double* dq,
+                              double* dk, double* dv, double* lse, int64_t nq, int64_t nk, int H, int D,
+                              int64_t group_q, int64_t group_k, double scale, const int64_t* rows, int64_t nrows,
+                              const int64_t* cols, int64_t ncols, int nthreads) {
+  if (H <= 0 || D <= 0 || nq <= 0 || nk <= 0) return -1;
+  if (group_q > 0 && (group_k <= 0 || nq % group_q != 0 || (nq / group_q) * group_k != nk)) return -1;
+  if (rows) {
+    for (int64_t i = 0; i < nrows; ++i)
+      if (rows[i] < 0 || rows[i] >= nq) return -1;
+  } else {
+    nrows = nq;
+  }
+  if (cols) {
+    for (int64_t i = 0; i < ncols; ++i)
+      if (cols[i] < 0 || cols[i] >= nk) return -1;
+  } else {
+    ncols = nk;
+  }
+  bwd_job J;
+  J.q = q; J.k = k; J.v = v; J.dout = dout;
+  J.dq = dq; J.dk = dk; J.dv = dv;
+  J.lse = lse;  /* [nq][H], filled by pass 1 */
+  J.csum = (double*)malloc(sizeof(double) * (size_t)(nq * H));
+  J.nq = nq; J.nk = nk; J.H = H; J.D = D;
+  J.group_q = group_q; J.group_k = group_k; J.scale = scale;
+  J.rows = rows; J.cols = cols; J.nrows = nrows; J.ncols = ncols;
+  pthread_mutex_init(&J.lock, NULL);
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > 256) nthreads = 256;
+  pthread_t th[256];
+  for (int phase = 1; phase <= 3; ++phase) {
+    J.phase = phase;
+    J.next = 0;
+    for (int i = 0; i < nthreads; ++i) pthread_create(&th[i], NULL, bwd_worker, &J);
+    for (int i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
+  }
+  pthread_mutex_destroy(&J.lock);
+  free(J.csum);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* FlashVGGT descriptor pooling                                             */
 /* ------------------------------------------------------------------------ */
 

@@ -433,6 +433,82 @@ def test_global_ex_extra_tokens_are_keys_and_queries_of_everything():
 
 
 # --------------------------------------------------------------------------
+# Attention gradients
+# --------------------------------------------------------------------------
+
+def _fd_grads(f, xs, dout, eps=1e-5):
+    """Central differences of L = sum(dout * f(*xs)) with respect to every input element."""
+    grads = []
+    for n in range(len(xs)):
+        g = np.zeros_like(xs[n])
+        it = np.nditer(xs[n], flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            plus = [x.copy() for x in xs]
+            minus = [x.copy() for x in xs]
+            plus[n][idx] += eps
+            minus[n][idx] -= eps
+            g[idx] = (np.sum(dout * f(*plus)) - np.sum(dout * f(*minus))) / (2 * eps)
+        grads.append(g)
+    return grads
+
+
+@pytest.mark.parametrize("frame", [False, True])
+def test_backward_matches_finite_differences_with_rope(frame):
+    r = _rng(60 + frame)
+    S, T, H, D = 2, 3, 1, 8
+    q, k, v = (r.standard_normal((S, T, H, D)) for _ in range(3))
+    dout = r.standard_normal((S * T, H, D))
+    pos = np.array([[0, 0], [1, 2], [3, 1]], dtype=np.int32)
+    fwd = oracle.frame_attn if frame else oracle.global_attn
+    bwd = oracle.frame_attn_backward if frame else oracle.global_attn_backward
+    fd = _fd_grads(lambda a, b, c: fwd(a, b, c, S, T, pos=pos, base=100.0), [q, k, v], dout.reshape(S * T, H, D))
+    dq, dk, dv, _ = bwd(q, k, v, dout, S, T, pos=pos, base=100.0)
+    for got, ref, name in ((dq, fd[0], "dq"), (dk, fd[1], "dk"), (dv, fd[2], "dv")):
+        np.testing.assert_allclose(got, ref.reshape(got.shape), rtol=1e-6, atol=1e-8, err_msg=name)
+
+
+def test_backward_against_torch_autograd():
+    import torch
+    r = _rng(62)
+    nq, nk, H, D = 7, 9, 2, 64
+    q, dout = r.standard_normal((nq, H, D)), r.standard_normal((nq, H, D))
+    k, v = r.standard_normal((nk, H, D)), r.standard_normal((nk, H, D))
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    s = torch.einsum("qhd,khd->hqk", tq, tk) * 0.125
+    o = torch.einsum("hqk,khd->qhd", torch.softmax(s, dim=-1), tv)
+    o.backward(torch.tensor(dout))
+    dq, dk, dv, lse = oracle.attention_backward(q, k, v, dout)
+    np.testing.assert_allclose(dq, tq.grad.numpy(), rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(lse, torch.logsumexp(s, dim=-1).T.detach().numpy(), rtol=1e-13)
+
+
+def test_backward_closed_forms():
+    r = _rng(63)
+    nq, nk, H, D = 6, 5, 2, 16
+    q, dout = r.standard_normal((nq, H, D)), r.standard_normal((nq, H, D))
+    k, v = r.standard_normal((nk, H, D)), r.standard_normal((nk, H, D))
+    dq, dk, dv, _ = oracle.attention_backward(q, k, v, dout)
+    # every softmax row's gradient sums to zero, so the key gradients cancel
+    np.testing.assert_allclose(dk.sum(axis=0), 0.0, atol=1e-13)
+    # every probability row sums to one, so the value gradients add up to dout
+    np.testing.assert_allclose(dv.sum(axis=0), dout.sum(axis=0), rtol=1e-12, atol=1e-13)
+    # one key: the output is that value whatever q and k are
+    dq1, dk1, dv1, _ = oracle.attention_backward(q, k[:1], v[:1], dout)
+    np.testing.assert_allclose(dq1, 0.0, atol=1e-15)
+    np.testing.assert_allclose(dk1, 0.0, atol=1e-15)
+    np.testing.assert_allclose(dv1[0], dout.sum(axis=0), rtol=1e-13)
+    # sampled query rows and key rows are the corresponding rows of the full result
+    rows, cols = np.array([5, 0, 3]), np.array([4, 1])
+    sq, sk, sv, _ = oracle.attention_backward(q, k, v, dout, rows=rows, cols=cols)
+    np.testing.assert_array_equal(sq, dq[rows])
+    np.testing.assert_array_equal(sk, dk[cols])
+    np.testing.assert_array_equal(sv, dv[cols])
+
+
+# --------------------------------------------------------------------------
 # Descriptor pooling and cross-attention
 # --------------------------------------------------------------------------
 
