@@ -71,6 +71,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stream", action="store_true", help="skip the FlashVGGT chunk-recursive measurement")
     ap.add_argument("--no-omega", action="store_true", help="skip the VGGT-Omega 64-frame measurement")
+    ap.add_argument("--no-backward", action="store_true", help="skip the attention-gradient measurement")
     ap.add_argument("--no-extras", action="store_true",
                     help="time only the headline step (no Q/K-norm, streaming or Omega sections)")
     ap.add_argument("--cpu-row-stride", type=int, default=48)
@@ -226,6 +227,8 @@ def main() -> int:
         result["qknorm"] = bench_qknorm(ffv, qd, kd, vd, posd, ws_g, ws_f, max(3, args.steps // 2), flops)
     if not (args.no_stream or args.no_extras):
         result["stream"] = bench_stream(ffv, dev, max(3, args.steps // 2), 2)
+    if not (args.no_backward or args.no_extras):
+        result["backward"] = bench_backward(ffv, qd, kd, vd, posd, max(3, args.steps // 4), flops)
     if not (args.no_omega or args.no_extras):
         result["omega"] = bench_omega(ffv, dev, max(3, args.steps // 4))
     if not args.no_cpu_baseline:
@@ -274,6 +277,56 @@ def bench_qknorm(ffv, qd, kd, vd, posd, ws_g, ws_f, iters, flops):
         out[f"{kind}_kernel_ms"] = round(float(np.mean(kern)), 4)
         out[f"{kind}_call_tflops"] = round(flops[kind] / (call_ms * 1e-3) / 1e12, 2)
     return out
+
+
+def bench_backward(ffv, qd, kd, vd, posd, iters, flops):
+    """Gradients of global attention on the same workload (RoPE on): the
+    training forward (output + log-normaliser) once, then the backward call
+    timed, and its dQ and dK/dV kernels by the library's kernel timer.
+    Algorithmic FLOP of the backward: the five N x N x 64 products of the
+    chain rule per head (S, dP, dV, dQ, dK) = 2.5 x the forward's 4*N*N*H*64;
+    the two kernels execute seven (S and dP are formed in both)."""
+    import torch
+
+    import workload
+
+    S, T, H = qd.shape[0], qd.shape[1], qd.shape[2]
+    dout = torch.from_numpy(workload.normal_bf16(0xBAC4, tuple(qd.shape)).view(np.int16)).to(qd.device).view(
+        torch.bfloat16)
+    o, lse = ffv.vggt_global_attn_train(qd, kd, vd, pos_yx=posd)
+    grads = tuple(torch.empty_like(qd) for _ in range(3))
+    ws = torch.empty(max(1, int(ffv.lib().vggt_attn_backward_workspace(S, T, H, 1, 1, 0))), dtype=torch.uint8,
+                     device=qd.device)
+    stream = torch.cuda.current_stream()
+
+    def call():
+        ffv.vggt_global_attn_backward(qd, kd, vd, o, dout, lse, pos_yx=posd, workspace=ws, grads=grads)
+
+    call()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    torch.cuda.synchronize()
+    ffv.vggt_timer_start(2 * iters)
+    for a, b in ev:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    kern = {}
+    for kind, ms in ffv.vggt_timer_stop():
+        kern.setdefault(kind, []).append(ms)
+    call_ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+    bwd_flops = 2.5 * flops["global"]
+    dq_ms, dkdv_ms = float(np.mean(kern["bwd_dq"])), float(np.mean(kern["bwd_dkdv"]))
+    return {
+        "workload": f"global attention gradients, S={S} x T={T}, H={H}, d=64, RoPE base 100, bf16",
+        "algorithmic_tflop": round(bwd_flops / 1e12, 3),
+        "call_ms": round(call_ms, 4),
+        "call_tflops": round(bwd_flops / (call_ms * 1e-3) / 1e12, 2),
+        "dq_kernel_ms": round(dq_ms, 4),
+        "dkdv_kernel_ms": round(dkdv_ms, 4),
+        "kernels_tflops": round(bwd_flops / ((dq_ms + dkdv_ms) * 1e-3) / 1e12, 2),
+        "kernels_frac_of_bf16_peak": round(bwd_flops / ((dq_ms + dkdv_ms) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+    }
 
 
 def bench_omega(ffv, dev, iters):

@@ -62,11 +62,16 @@ SIGNATURES = {
     "vggt_global_attn_ex_workspace": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i]),
     "vggt_global_attn_ex": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _vp, _f, _f, _i,
                                  _np, _vp, _sz, _vp]),
+    "vggt_frame_attn_train": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _f, _f, _vp, _sz, _vp]),
+    "vggt_global_attn_train": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _f, _f, _i, _vp, _sz, _vp]),
+    "vggt_attn_backward_workspace": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "vggt_frame_attn_backward": (_i, [_vp] * 9 + [_i, _i, _i, _i, _vp, _f, _f, _vp, _sz, _vp]),
+    "vggt_global_attn_backward": (_i, [_vp] * 9 + [_i, _i, _i, _i, _vp, _f, _f, _vp, _sz, _vp]),
     "vggt_timer_start": (_i, [_i]),
     "vggt_timer_stop": (_i, [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(_i), _i, ctypes.POINTER(_i)]),
 }
 
-TIMER_KINDS = {1: "frame", 2: "global", 3: "xattn", 4: "cache", 5: "chunked"}
+TIMER_KINDS = {1: "frame", 2: "global", 3: "xattn", 4: "cache", 5: "chunked", 6: "bwd_dq", 7: "bwd_dkdv"}
 
 _lib = None
 
@@ -297,6 +302,62 @@ def vggt_global_attn_ex(q, k, v, T_active, xq=None, xk=None, xv=None, out=None, 
                                      _ptr(xout if E else None), E, _pos(pos_yx, T), rope_base, scale, kv_splits,
                                      norm, _ptr(ws), nbytes, _stream(stream)))
     return out, (xout if E else None)
+
+
+def vggt_frame_attn_train(q, k, v, out=None, lse=None, pos_yx=None, rope_base=100.0, scale=0.0, workspace=None,
+                          stream=None):
+    """Frame attention that also returns the log-normaliser lse [S*T, H] (float32); returns (out, lse)."""
+    S, T, H, out = _check_qkv(q, k, v, out)
+    lse = torch.empty((S * T, H), dtype=torch.float32, device=q.device) if lse is None else lse
+    need = vggt_frame_attn_workspace(S, T, H, pos_yx is not None, q.dtype)
+    ws, nbytes = _workspace(need, q.device, workspace)
+    _check("vggt_frame_attn_train",
+           lib().vggt_frame_attn_train(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _dtype_code(q), S, T, H,
+                                       _pos(pos_yx, T), rope_base, scale, _ptr(ws), nbytes, _stream(stream)))
+    return out, lse
+
+
+def vggt_global_attn_train(q, k, v, out=None, lse=None, pos_yx=None, rope_base=100.0, scale=0.0, kv_splits=0,
+                           workspace=None, stream=None):
+    """Global attention that also returns the log-normaliser lse [S*T, H] (float32); returns (out, lse)."""
+    S, T, H, out = _check_qkv(q, k, v, out)
+    lse = torch.empty((S * T, H), dtype=torch.float32, device=q.device) if lse is None else lse
+    need = vggt_global_attn_workspace(S, T, H, kv_splits, pos_yx is not None, q.dtype)
+    ws, nbytes = _workspace(need, q.device, workspace)
+    _check("vggt_global_attn_train",
+           lib().vggt_global_attn_train(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _dtype_code(q), S, T, H,
+                                        _pos(pos_yx, T), rope_base, scale, kv_splits, _ptr(ws), nbytes,
+                                        _stream(stream)))
+    return out, lse
+
+
+def _backward(name, global_, q, k, v, out, dout, lse, pos_yx, rope_base, scale, workspace, stream, grads):
+    S, T, H, _ = _check_qkv(q, k, v, out)
+    if tuple(dout.shape) != tuple(q.shape) or dout.dtype != q.dtype or not dout.is_contiguous():
+        raise ValueError("dout must match q")
+    if lse.dtype != torch.float32 or lse.numel() != S * T * H or not lse.is_contiguous():
+        raise ValueError(f"lse must be contiguous float32 of {S * T * H} elements")
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3)) if grads is None else grads
+    need = int(lib().vggt_attn_backward_workspace(S, T, H, int(global_), int(pos_yx is not None), _dtype_code(q)))
+    ws, nbytes = _workspace(need, q.device, workspace)
+    _check(name, getattr(lib(), name)(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+                                      _ptr(dv), _dtype_code(q), S, T, H, _pos(pos_yx, T), rope_base, scale, _ptr(ws),
+                                      nbytes, _stream(stream)))
+    return dq, dk, dv
+
+
+def vggt_frame_attn_backward(q, k, v, out, dout, lse, pos_yx=None, rope_base=100.0, scale=0.0, workspace=None,
+                             stream=None, grads=None):
+    """Gradients (dq, dk, dv) of frame attention from the training forward's out and lse."""
+    return _backward("vggt_frame_attn_backward", False, q, k, v, out, dout, lse, pos_yx, rope_base, scale, workspace,
+                     stream, grads)
+
+
+def vggt_global_attn_backward(q, k, v, out, dout, lse, pos_yx=None, rope_base=100.0, scale=0.0, workspace=None,
+                              stream=None, grads=None):
+    """Gradients (dq, dk, dv) of global attention from the training forward's out and lse."""
+    return _backward("vggt_global_attn_backward", True, q, k, v, out, dout, lse, pos_yx, rope_base, scale, workspace,
+                     stream, grads)
 
 
 def vggt_descriptor_count(T, gh, gw, ph, pw) -> int:

@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libvggt_attn.so")
 
-SOURCES = ["capi.cpp", "attn_bf16.hip", "attn_f32.hip", "merge.hip", "rope.hip", "prep.hip", "pool.hip"]
+SOURCES = ["capi.cpp", "attn_bf16.hip", "attn_f32.hip", "attn_bwd.hip", "merge.hip", "rope.hip", "prep.hip", "pool.hip"]
 
 
 def hipcc() -> str:

@@ -66,6 +66,7 @@ constexpr int NSTAGE = 4;         // LDS ring depth (tiles in flight = NSTAGE - 
 constexpr float kSumLimit = 18446744073709551616.0f;  // 2^64
 constexpr float kRaise = 32.0f;   // move m when a tile max exceeds it by this
 constexpr float kLow = -64.0f;    // first tile: move m down when the max is below this
+constexpr float kLn2 = 0.693147180559945309f;
 
 __device__ __forceinline__ int rho(int i) { return (i & ~0xC) | ((i & 4) << 1) | ((i & 8) >> 1); }
 __device__ __forceinline__ int vt_swz(int d) { return (d ^ (d >> 3)) & 7; }
@@ -78,12 +79,6 @@ struct Smem {
   u32x4 k[NSTAGE][BK][8];
   u32x4 vt[NSTAGE][D][8];
 };
-
-__device__ __forceinline__ void xcd_remap(int w, int nwg, int& logical) {
-  const int q = nwg >> 3, r = nwg & 7;
-  const int xcd = w & 7, k = w >> 3;
-  logical = (xcd < r) ? xcd * (q + 1) + k : r * (q + 1) + (xcd - r) * q + k;
-}
 
 __device__ __forceinline__ float dot2_acc(uint32_t pk, float acc) {
   const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
@@ -437,6 +432,7 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
     if (qi >= nq_seq) continue;
     if (p.splits == 1) {
       const float inv = 1.0f / ltot;
+      if (p.lse && hi == 0) p.lse[(seq * p.q_seq_stride + qi) * p.H + head] = (mref[qb] + log2f(ltot)) * kLn2;
       uint16_t* og = (uint16_t*)p.o + (seq * p.q_seq_stride + qi) * p.tok_stride + head * D;
 #pragma unroll
       for (int db = 0; db < 2; ++db)

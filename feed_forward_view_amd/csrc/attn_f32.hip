@@ -91,6 +91,7 @@ __global__ __launch_bounds__(NT) void attn_fwd_f32_kernel(AttnProblem p) {
 
   if (!valid) return;
   if (p.splits == 1) {
+    if (p.lse) p.lse[(seq * p.q_seq_stride + qi) * p.H + head] = (m + log2f(l)) * 0.693147180559945309f;
     float* og = (float*)p.o + (seq * p.q_seq_stride + qi) * p.tok_stride + head * D;
 #pragma unroll
     for (int d = 0; d < D; d += 4) {

@@ -395,9 +395,17 @@ vggt_status check_norm_alias(const vggt_qk_norm* n, const void* o, size_t o_byte
   return VGGT_OK;
 }
 
+vggt_status check_lse(float* lse, size_t lse_bytes, const void* const* others, const size_t* sizes, int n) {
+  if (!lse) return fail(VGGT_ERR_NULL, "lse is required");
+  if (reinterpret_cast<uintptr_t>(lse) & 3u) return fail(VGGT_ERR_ALIGN, "lse must be 4-byte aligned");
+  for (int i = 0; i < n; ++i)
+    if (overlap(lse, lse_bytes, others[i], sizes[i])) return fail(VGGT_ERR_ALIAS, "lse overlaps another buffer");
+  return VGGT_OK;
+}
+
 vggt_status frame_attn(const void* q, const void* k, const void* v, void* o, vggt_dtype dt, int S, int T, int H,
                        const int32_t* pos_yx, float rope_base, float scale, const vggt_qk_norm* norm, void* workspace,
-                       size_t ws_bytes, void* stream) {
+                       size_t ws_bytes, void* stream, float* lse = nullptr, bool want_lse = false) {
   g_last_error[0] = 0;
   if (!dtype_ok(dt)) return fail(VGGT_ERR_UNSUPPORTED, "unknown dtype %d", (int)dt);
   if (!tokens_ok(S, T, H)) return fail(VGGT_ERR_SHAPE, "bad shape S=%d T=%d H=%d", S, T, H);
@@ -408,16 +416,23 @@ vggt_status frame_attn(const void* q, const void* k, const void* v, void* o, vgg
   if (vggt_status s = validate_attn({q, k, v, o}, pos_yx, rope_base, L.total, workspace, ws_bytes, bytes, bytes))
     return s;
   if (vggt_status s = check_norm_alias(norm, o, bytes, workspace, L.total)) return s;
+  if (want_lse) {
+    const void* others[] = {q, k, v, o, workspace};
+    const size_t sizes[] = {bytes, bytes, bytes, bytes, L.total};
+    if (vggt_status s = check_lse(lse, (size_t)S * T * H * 4, others, sizes, 5)) return s;
+  }
   if (vggt_status s = check_device()) return s;
-  hipError_t e = run_call(L, base_problem(q, k, v, o, H, scale), dt, S, T, T, pos_yx, rope_base, T,
-                          (char*)workspace, (hipStream_t)stream, VGGT_TIMER_FRAME, norm);
+  vggt::AttnProblem p = base_problem(q, k, v, o, H, scale);
+  p.lse = lse;
+  hipError_t e = run_call(L, p, dt, S, T, T, pos_yx, rope_base, T, (char*)workspace, (hipStream_t)stream,
+                          VGGT_TIMER_FRAME, norm);
   if (e != hipSuccess) return device_error("frame attention launch", e);
   return VGGT_OK;
 }
 
 vggt_status global_attn(const void* q, const void* k, const void* v, void* o, vggt_dtype dt, int S, int T, int H,
                         const int32_t* pos_yx, float rope_base, float scale, int kv_splits, const vggt_qk_norm* norm,
-                        void* workspace, size_t ws_bytes, void* stream) {
+                        void* workspace, size_t ws_bytes, void* stream, float* lse = nullptr, bool want_lse = false) {
   g_last_error[0] = 0;
   if (!dtype_ok(dt)) return fail(VGGT_ERR_UNSUPPORTED, "unknown dtype %d", (int)dt);
   if (!tokens_ok(S, T, H)) return fail(VGGT_ERR_SHAPE, "bad shape S=%d T=%d H=%d", S, T, H);
@@ -430,9 +445,16 @@ vggt_status global_attn(const void* q, const void* k, const void* v, void* o, vg
   if (vggt_status s = validate_attn({q, k, v, o}, pos_yx, rope_base, L.total, workspace, ws_bytes, bytes, bytes))
     return s;
   if (vggt_status s = check_norm_alias(norm, o, bytes, workspace, L.total)) return s;
+  if (want_lse) {
+    const void* others[] = {q, k, v, o, workspace};
+    const size_t sizes[] = {bytes, bytes, bytes, bytes, L.total};
+    if (vggt_status s = check_lse(lse, (size_t)N * H * 4, others, sizes, 5)) return s;
+  }
   if (vggt_status s = check_device()) return s;
-  hipError_t e = run_call(L, base_problem(q, k, v, o, H, scale), dt, 1, N, N, pos_yx, rope_base, T,
-                          (char*)workspace, (hipStream_t)stream, VGGT_TIMER_GLOBAL, norm);
+  vggt::AttnProblem p = base_problem(q, k, v, o, H, scale);
+  p.lse = lse;
+  hipError_t e = run_call(L, p, dt, 1, N, N, pos_yx, rope_base, T, (char*)workspace, (hipStream_t)stream,
+                          VGGT_TIMER_GLOBAL, norm);
   if (e != hipSuccess) return device_error("global attention launch", e);
   return VGGT_OK;
 }
@@ -1034,4 +1056,237 @@ VGGT_API vggt_status vggt_global_attn_ex(const void* q, const void* k, const voi
                                          void* stream) {
   const ExArgs a{true, q, k, v, o, xq, xk, xv, xo, S, T, T_active, n_extra, H, pos_yx, rope_base, scale, norm};
   return ex_call(a, dt, kv_splits, workspace, ws_bytes, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Training: forward with the log-normaliser, and the gradients
+// ---------------------------------------------------------------------------
+
+VGGT_API vggt_status vggt_frame_attn_train(const void* q, const void* k, const void* v, void* o, float* lse,
+                                           vggt_dtype dt, int S, int T, int H, const int32_t* pos_yx,
+                                           float rope_base, float scale, void* workspace, size_t ws_bytes,
+                                           void* stream) {
+  return frame_attn(q, k, v, o, dt, S, T, H, pos_yx, rope_base, scale, nullptr, workspace, ws_bytes, stream, lse,
+                    true);
+}
+
+VGGT_API vggt_status vggt_global_attn_train(const void* q, const void* k, const void* v, void* o, float* lse,
+                                            vggt_dtype dt, int S, int T, int H, const int32_t* pos_yx,
+                                            float rope_base, float scale, int kv_splits, void* workspace,
+                                            size_t ws_bytes, void* stream) {
+  return global_attn(q, k, v, o, dt, S, T, H, pos_yx, rope_base, scale, kv_splits, nullptr, workspace, ws_bytes,
+                     stream, lse, true);
+}
+
+namespace {
+
+// Workspace of one backward call.  bf16: RoPE table, rotated copies of Q and K,
+// seven tile sets (K rows, V rows, K^T, scaled Q rows, dO rows, Q^T, dO^T) and
+// the per-row statistics; fp32: rotated copies and rotated-frame gradients.
+struct BwdLayout {
+  size_t table = 0, qr = 0, kr = 0, tiles[7] = {0, 0, 0, 0, 0, 0, 0}, lse2 = 0, dsum = 0, dqr = 0, dkr = 0;
+  size_t total = 0;
+  int nseq = 1, n = 0, ntile = 0;
+};
+
+void add_b(BwdLayout& L, size_t& off, size_t bytes) {
+  off = L.total;
+  L.total += align256(bytes);
+}
+
+BwdLayout plan_bwd(bool global, int S, int T, int H, bool rope, vggt_dtype dt) {
+  BwdLayout L;
+  L.nseq = global ? 1 : S;
+  L.n = global ? S * T : T;
+  L.ntile = (L.n + 63) / 64;
+  const size_t tensor = (size_t)S * T * H * vggt::kHeadDim * elem_size(dt);
+  if (dt == VGGT_BF16) {
+    if (rope) {
+      add_b(L, L.table, (size_t)T * 32 * 8);
+      add_b(L, L.qr, tensor);
+      add_b(L, L.kr, tensor);
+    }
+    const size_t tiles = (size_t)L.nseq * H * L.ntile * 64 * vggt::kHeadDim * 2;
+    for (size_t& t : L.tiles) add_b(L, t, tiles);
+  } else if (rope) {
+    add_b(L, L.qr, tensor);
+    add_b(L, L.kr, tensor);
+    add_b(L, L.dqr, tensor);
+    add_b(L, L.dkr, tensor);
+  }
+  const size_t stats = (size_t)L.nseq * H * L.ntile * 64 * 4;
+  add_b(L, L.lse2, stats);
+  add_b(L, L.dsum, stats);
+  return L;
+}
+
+vggt_status attn_backward(bool global, const void* q, const void* k, const void* v, const void* o, const void* dout,
+                          const float* lse, void* dq, void* dk, void* dv, vggt_dtype dt, int S, int T, int H,
+                          const int32_t* pos, float base, float scale, void* workspace, size_t ws_bytes,
+                          void* stream) {
+  g_last_error[0] = 0;
+  if (!dtype_ok(dt)) return fail(VGGT_ERR_UNSUPPORTED, "unknown dtype %d", (int)dt);
+  if (!tokens_ok(S, T, H)) return fail(VGGT_ERR_SHAPE, "bad shape S=%d T=%d H=%d", S, T, H);
+  if (pos && (!(base > 0.0f) || !std::isfinite(base))) return fail(VGGT_ERR_SHAPE, "rope base must be finite and > 0");
+  if (S == 0) return VGGT_OK;
+  const void* in[] = {q, k, v, o, dout};
+  void* out[] = {dq, dk, dv};
+  for (const void* t : in)
+    if (!t) return fail(VGGT_ERR_NULL, "q, k, v, o and dout are required");
+  for (const void* t : out)
+    if (!t) return fail(VGGT_ERR_NULL, "dq, dk and dv are required");
+  if (!lse) return fail(VGGT_ERR_NULL, "lse is required");
+  for (const void* t : in)
+    if (!aligned16(t)) return fail(VGGT_ERR_ALIGN, "tensors must be 16-byte aligned");
+  for (const void* t : out)
+    if (!aligned16(t)) return fail(VGGT_ERR_ALIGN, "tensors must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(lse) & 3u) || (pos && (reinterpret_cast<uintptr_t>(pos) & 3u)))
+    return fail(VGGT_ERR_ALIGN, "lse and pos_yx must be 4-byte aligned");
+  const size_t bytes = (size_t)S * T * H * vggt::kHeadDim * elem_size(dt);
+  const size_t lse_b = (size_t)S * T * H * 4;
+  const BwdLayout L = plan_bwd(global, S, T, H, pos != nullptr, dt);
+  if (!workspace) return fail(VGGT_ERR_WORKSPACE, "workspace of %zu bytes required", L.total);
+  if (ws_bytes < L.total) return fail(VGGT_ERR_WORKSPACE, "workspace %zu < required %zu bytes", ws_bytes, L.total);
+  if (!aligned16(workspace)) return fail(VGGT_ERR_ALIGN, "workspace must be 16-byte aligned");
+  for (int i = 0; i < 3; ++i) {
+    for (const void* t : in)
+      if (overlap(out[i], bytes, t, bytes)) return fail(VGGT_ERR_ALIAS, "a gradient overlaps an input");
+    if (overlap(out[i], bytes, lse, lse_b) || overlap(out[i], bytes, workspace, L.total))
+      return fail(VGGT_ERR_ALIAS, "a gradient overlaps lse or the workspace");
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(out[i], bytes, out[j], bytes)) return fail(VGGT_ERR_ALIAS, "gradients overlap each other");
+  }
+  for (const void* t : in)
+    if (overlap(workspace, L.total, t, bytes)) return fail(VGGT_ERR_ALIAS, "workspace overlaps an input");
+  if (overlap(workspace, L.total, lse, lse_b)) return fail(VGGT_ERR_ALIAS, "workspace overlaps lse");
+  if (vggt_status s = check_device()) return s;
+
+  char* ws = (char*)workspace;
+  const hipStream_t st = (hipStream_t)stream;
+  const int64_t N = (int64_t)S * T;
+  const float c = scale_log2(scale);
+  const float sc = scale > 0.0f ? scale : 0.125f;
+  hipError_t e = hipSuccess;
+  float* lse2 = (float*)(ws + L.lse2);
+  float* dsum = (float*)(ws + L.dsum);
+  const int64_t seq_stride = global ? 0 : T;
+  e = vggt::launch_attn_bwd_pre(o, dout, dt == VGGT_BF16, lse, lse2, dsum, L.nseq, L.n, seq_stride, H, L.ntile, st);
+  if (e != hipSuccess) return device_error("backward pre-pass", e);
+  if (dt == VGGT_BF16) {
+    const void* table = nullptr;
+    const void* qr = q;
+    const void* kr = k;
+    if (pos) {
+      e = vggt::launch_rope_table(pos, T, (double)base, ws + L.table, st);
+      if (e == hipSuccess) e = vggt::launch_rope(q, ws + L.qr, true, N, T, H, pos, (double)base, st);
+      if (e == hipSuccess) e = vggt::launch_rope(k, ws + L.kr, true, N, T, H, pos, (double)base, st);
+      if (e != hipSuccess) return device_error("backward rotation", e);
+      table = ws + L.table;
+      qr = ws + L.qr;
+      kr = ws + L.kr;
+    }
+    char* tk = ws + L.tiles[0];
+    char* tv = ws + L.tiles[1];
+    char* tkt = ws + L.tiles[2];
+    char* tq = ws + L.tiles[3];
+    char* tdo = ws + L.tiles[4];
+    char* tqt = ws + L.tiles[5];
+    char* tdot = ws + L.tiles[6];
+    const int n = L.n, ns = L.nseq;
+    e = vggt::launch_k_tiles_bf16(vggt::contiguous_keys(k, n), tk, ns, n, H, table, T, nullptr, nullptr, 0.0f, st);
+    if (e == hipSuccess)
+      e = vggt::launch_k_tiles_bf16(vggt::contiguous_keys(v, n), tv, ns, n, H, nullptr, 1, nullptr, nullptr, 0.0f, st);
+    if (e == hipSuccess) e = vggt::launch_v_tiles_bf16(vggt::contiguous_keys(kr, n), tkt, ns, n, H, st);
+    if (e == hipSuccess)
+      e = vggt::launch_k_tiles_bf16(vggt::contiguous_keys(q, n), tq, ns, n, H, table, T, nullptr, nullptr, 0.0f, st,
+                                    c);
+    if (e == hipSuccess)
+      e = vggt::launch_k_tiles_bf16(vggt::contiguous_keys(dout, n), tdo, ns, n, H, nullptr, 1, nullptr, nullptr, 0.0f,
+                                    st);
+    if (e == hipSuccess) e = vggt::launch_v_tiles_bf16(vggt::contiguous_keys(qr, n), tqt, ns, n, H, st);
+    if (e == hipSuccess) e = vggt::launch_v_tiles_bf16(vggt::contiguous_keys(dout, n), tdot, ns, n, H, st);
+    if (e != hipSuccess) return device_error("backward tile pre-pass", e);
+    vggt::AttnBwdProblem p;
+    std::memset(&p, 0, sizeof(p));
+    p.q = q;
+    p.dout = dout;
+    p.kr = kr;
+    p.v = v;
+    p.rope_tab = (const vggt::f32x2*)table;
+    p.rope_T = T;
+    p.k_rows = tk;
+    p.v_rows = tv;
+    p.k_trans = tkt;
+    p.q_rows = tq;
+    p.do_rows = tdo;
+    p.q_trans = tqt;
+    p.do_trans = tdot;
+    p.lse2 = lse2;
+    p.dsum = dsum;
+    p.dq = dq;
+    p.dk = dk;
+    p.dv = dv;
+    p.tok_stride = (int64_t)H * vggt::kHeadDim;
+    p.seq_stride = seq_stride;
+    p.nseq = ns;
+    p.n = n;
+    p.H = H;
+    p.ntile = L.ntile;
+    p.scale_log2 = c;
+    p.scale = sc;
+    for (int pass = 0; pass < 2; ++pass) {
+      const int slot = timer_claim(pass == 0 ? VGGT_TIMER_BWD_DQ : VGGT_TIMER_BWD_DKDV);
+      if (slot >= 0) e = hipEventRecord(g_timer.ev[2 * slot], st);
+      if (e == hipSuccess) e = vggt::launch_attn_bwd_bf16(p, pass == 0, st);
+      if (e == hipSuccess && slot >= 0) e = hipEventRecord(g_timer.ev[2 * slot + 1], st);
+      if (e != hipSuccess) return device_error("backward launch", e);
+    }
+    return VGGT_OK;
+  }
+  // fp32 debug path
+  const float* qr = (const float*)q;
+  const float* kr = (const float*)k;
+  float* dqr = (float*)dq;
+  float* dkr = (float*)dk;
+  if (pos) {
+    e = vggt::launch_rope(q, ws + L.qr, false, N, T, H, pos, (double)base, st);
+    if (e == hipSuccess) e = vggt::launch_rope(k, ws + L.kr, false, N, T, H, pos, (double)base, st);
+    if (e != hipSuccess) return device_error("backward rotation", e);
+    qr = (const float*)(ws + L.qr);
+    kr = (const float*)(ws + L.kr);
+    dqr = (float*)(ws + L.dqr);
+    dkr = (float*)(ws + L.dkr);
+  }
+  e = vggt::launch_attn_bwd_f32(qr, kr, (const float*)v, (const float*)dout, lse2, dsum, dqr, dkr, (float*)dv, L.nseq,
+                                L.n, seq_stride, H, L.ntile, c, sc, st);
+  if (e == hipSuccess && pos) e = vggt::launch_rope(dqr, dq, false, N, T, H, pos, (double)base, st, true);
+  if (e == hipSuccess && pos) e = vggt::launch_rope(dkr, dk, false, N, T, H, pos, (double)base, st, true);
+  if (e != hipSuccess) return device_error("backward launch", e);
+  return VGGT_OK;
+}
+
+}  // namespace
+
+VGGT_API size_t vggt_attn_backward_workspace(int S, int T, int H, int global, int rope_on, vggt_dtype dt) {
+  if (!dtype_ok(dt) || !tokens_ok(S, T, H)) return 0;
+  if (S == 0) return 0;
+  return plan_bwd(global != 0, S, T, H, rope_on != 0, dt).total;
+}
+
+VGGT_API vggt_status vggt_frame_attn_backward(const void* q, const void* k, const void* v, const void* o,
+                                              const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                                              vggt_dtype dt, int S, int T, int H, const int32_t* pos_yx,
+                                              float rope_base, float scale, void* workspace, size_t ws_bytes,
+                                              void* stream) {
+  return attn_backward(false, q, k, v, o, dout, lse, dq, dk, dv, dt, S, T, H, pos_yx, rope_base, scale, workspace,
+                       ws_bytes, stream);
+}
+
+VGGT_API vggt_status vggt_global_attn_backward(const void* q, const void* k, const void* v, const void* o,
+                                               const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                                               vggt_dtype dt, int S, int T, int H, const int32_t* pos_yx,
+                                               float rope_base, float scale, void* workspace, size_t ws_bytes,
+                                               void* stream) {
+  return attn_backward(true, q, k, v, o, dout, lse, dq, dk, dv, dt, S, T, H, pos_yx, rope_base, scale, workspace,
+                       ws_bytes, stream);
 }

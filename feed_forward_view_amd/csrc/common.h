@@ -27,6 +27,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
+// Workgroups are dealt round-robin to the 8 XCDs; this maps the hardware id w
+// of nwg workgroups to a logical id such that each XCD receives a contiguous
+// run of logical ids (consecutive work shares that XCD's L2).
+__device__ __forceinline__ void xcd_remap(int w, int nwg, int& logical) {
+  const int q = nwg >> 3, r = nwg & 7;
+  const int xcd = w & 7, k = w >> 3;
+  logical = (xcd < r) ? xcd * (q + 1) + k : r * (q + 1) + (xcd - r) * q + k;
+}
+
 // One attention problem as the kernels see it.  Q/K/V/O are [tokens][H][64];
 // queries of sequence `s` are tokens [s*q_seq_stride, s*q_seq_stride + nq),
 // its keys are tokens [s*k_seq_stride, s*k_seq_stride + nk).  With
@@ -61,7 +70,52 @@ struct AttnProblem {
   const float* q_ln_g;     // bf16 kernel: per-head LayerNorm of Q before RoPE (gamma [64]), or null
   const float* q_ln_b;     // beta [64]
   float ln_eps;
+  float* lse;              // or null: natural log-normaliser of every query row, [token][H]
 };
+
+// Attention gradients (bf16).  Sequences, strides and counts as in
+// AttnProblem with nq == nk and q/k sequences T tokens apart (frame) or one
+// sequence (global).  Tile buffers: [nseq][H][ntile][64 x 64] in the forward
+// kernel's layouts -- "row" tiles as its K tiles (rows in key order rho),
+// "transposed" tiles as its V^T tiles.
+struct AttnBwdProblem {
+  const void* q;           // [tokens][H][64] bf16: Q fragments of the dQ kernel
+  const void* dout;        // [tokens][H][64] bf16: dO fragments of the dQ kernel
+  const void* kr;          // K rotated (bf16): key fragments of the dK/dV kernel
+  const void* v;           // V: value fragments of the dK/dV kernel
+  const f32x2* rope_tab;   // [rope_T][32] cos/sin or null
+  int rope_T;
+  const void* k_rows;      // K rotated, row tiles (the forward's K tiles)
+  const void* v_rows;      // V, row tiles
+  const void* k_trans;     // K rotated, transposed tiles
+  const void* q_rows;      // Q rotated and scaled by scale*log2(e), row tiles
+  const void* do_rows;     // dO, row tiles
+  const void* q_trans;     // Q rotated, transposed tiles
+  const void* do_trans;    // dO, transposed tiles
+  const float* lse2;       // [nseq][H][ntile*64]: log2-normaliser of each query row (+inf past the end)
+  const float* dsum;       // [nseq][H][ntile*64]: rowsum(dO * O) (0 past the end)
+  void* dq;                // [tokens][H][64] bf16 outputs
+  void* dk;
+  void* dv;
+  int64_t tok_stride;      // H*64
+  int64_t seq_stride;      // tokens between sequence starts (0 for one sequence)
+  int nseq, n, H, ntile;   // n tokens per sequence, ntile = ceil(n / 64)
+  float scale_log2;        // scale * log2(e)
+  float scale;
+};
+
+// dq: the dQ kernel, else the dK/dV kernel.
+hipError_t launch_attn_bwd_bf16(const AttnBwdProblem& p, bool dq, hipStream_t stream);
+// lse2 / dsum of the backward pass from the forward's lse and rowsum(dO * O);
+// rows [nseq][H][ntile*64] padded with (+inf, 0).
+hipError_t launch_attn_bwd_pre(const void* o, const void* dout, bool bf16, const float* lse, float* lse2,
+                               float* dsum, int nseq, int n, int64_t seq_stride, int H, int ntile,
+                               hipStream_t stream);
+// fp32 debug gradients: one thread per (row, head); q/k already rotated.
+hipError_t launch_attn_bwd_f32(const float* qr, const float* kr, const float* v, const float* dout,
+                               const float* lse2, const float* dsum, float* dqr, float* dkr, float* dv, int nseq,
+                               int n, int64_t seq_stride, int H, int ntile, float scale_log2, float scale,
+                               hipStream_t stream);
 
 // Launchers (stream-ordered, no synchronisation).  Return hipSuccess or the
 // launch error.
@@ -69,7 +123,7 @@ hipError_t launch_attn_bf16(const AttnProblem& p, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnProblem& p, hipStream_t stream);
 hipError_t launch_attn_merge(const AttnProblem& p, bool out_bf16, hipStream_t stream);
 hipError_t launch_rope(const void* src, void* dst, bool bf16, int64_t n_tok, int T, int H, const int32_t* pos_yx,
-                       double base, hipStream_t stream);
+                       double base, hipStream_t stream, bool inverse = false);
 hipError_t launch_rope_table(const int32_t* pos_yx, int T, double base, void* table, hipStream_t stream);
 // Where key j (0 <= j < len) of sequence s lives: keys [0, n_main) are rows of
 // `main` -- row s*seq_rows + j, or, with frame_len > 0, row s*seq_rows +
@@ -94,7 +148,8 @@ inline KeySrc contiguous_keys(const void* k, int len) {
 // K -> tiles for nseq sequences of len keys (RoPE position of a main row r is
 // r % rope_T; extra rows are not rotated), with an optional per-head LayerNorm.
 hipError_t launch_k_tiles_bf16(const KeySrc& k, void* kt, int nseq, int len, int H, const void* table, int rope_T,
-                               const float* ln_g, const float* ln_b, float ln_eps, hipStream_t stream);
+                               const float* ln_g, const float* ln_b, float ln_eps, hipStream_t stream,
+                               float out_scale = 1.0f);
 // Per-head LayerNorm of fp32 [n_tok][H][64] (src may equal dst).
 hipError_t launch_layer_norm_f32(const float* src, float* dst, int64_t n_tok, int H, const float* g, const float* b,
                                  float eps, hipStream_t stream);

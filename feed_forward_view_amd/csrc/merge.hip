@@ -45,6 +45,7 @@ __global__ __launch_bounds__(NT) void attn_merge_kernel(AttnProblem p) {
   }
   const int64_t seq = row / p.nq, qi = row % p.nq;
   const int64_t off = (seq * p.q_seq_stride + qi) * p.tok_stride + (int64_t)head * D + 8 * dc;
+  if (p.lse && dc == 0) p.lse[(seq * p.q_seq_stride + qi) * p.H + head] = (M + log2f(L)) * 0.693147180559945309f;
   if (OUT_BF16) {
     const u32x4 w = {pack_bf16x2(acc[0] / L, acc[1] / L), pack_bf16x2(acc[2] / L, acc[3] / L),
                      pack_bf16x2(acc[4] / L, acc[5] / L), pack_bf16x2(acc[6] / L, acc[7] / L)};

@@ -55,11 +55,13 @@ __device__ __forceinline__ int swz_vt(int d) { return (d ^ (d >> 3)) & 7; }
 //
 // With ln_g, every key's head vector is first centred and scaled by its per-head
 // LayerNorm (gamma ln_g, beta ln_b, eps ln_eps; the 8 lanes that hold one key row
-// reduce its 64 channels by xor shuffles), then rotated, then rounded once to bf16.
+// reduce its 64 channels by xor shuffles), then rotated, then multiplied by out_scale
+// and rounded once to bf16.
 __global__ __launch_bounds__(NT) void k_tiles_kernel(KeySrc k, u32x4* __restrict__ kt_out,
                                                      int len, int H, const f32x2* __restrict__ table, int rope_T,
                                                      int key0, int dst_ntile, const float* __restrict__ ln_g,
-                                                     const float* __restrict__ ln_b, float ln_eps) {
+                                                     const float* __restrict__ ln_b, float ln_eps,
+                                                     float out_scale) {
   const int tile = key0 / 64 + blockIdx.x, h = blockIdx.y, sq = blockIdx.z;
   u32x4* dst = kt_out + (((int64_t)sq * H + h) * dst_ntile + tile) * 512;
   const int64_t tok_stride = (int64_t)H * kHeadDim;
@@ -74,7 +76,7 @@ __global__ __launch_bounds__(NT) void k_tiles_kernel(KeySrc k, u32x4* __restrict
     if (key < len) {
       const int64_t row = key_row(k, sq, key);
       w = *(const u32x4*)(key_ptr<uint16_t>(k, row, tok_stride) + h * kHeadDim + 8 * u);
-      if (ln_g || (table && row >= 0)) {
+      if (ln_g || (table && row >= 0) || out_scale != 1.0f) {
         float f[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -113,7 +115,7 @@ __global__ __launch_bounds__(NT) void k_tiles_kernel(KeySrc k, u32x4* __restrict
           }
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(f[2 * e], f[2 * e + 1]);
+        for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(f[2 * e] * out_scale, f[2 * e + 1] * out_scale);
       }
     }
     dst[i] = w;
@@ -194,11 +196,12 @@ hipError_t launch_rope_table(const int32_t* pos_yx, int T, double base, void* ta
 }
 
 hipError_t launch_k_tiles_bf16(const KeySrc& k, void* kt, int nseq, int len, int H, const void* table, int rope_T,
-                               const float* ln_g, const float* ln_b, float ln_eps, hipStream_t stream) {
+                               const float* ln_g, const float* ln_b, float ln_eps, hipStream_t stream,
+                               float out_scale) {
   if (nseq <= 0 || len <= 0) return hipSuccess;
   const int ntile = (len + 63) / 64;
   hipLaunchKernelGGL(k_tiles_kernel, dim3((unsigned)ntile, (unsigned)H, (unsigned)nseq), dim3(NT), 0, stream, k,
-                     (u32x4*)kt, len, H, (const f32x2*)table, rope_T, 0, ntile, ln_g, ln_b, ln_eps);
+                     (u32x4*)kt, len, H, (const f32x2*)table, rope_T, 0, ntile, ln_g, ln_b, ln_eps, out_scale);
   return hipGetLastError();
 }
 
@@ -224,7 +227,7 @@ hipError_t launch_tiles_append_bf16(const void* k, const void* v, void* kt, void
   const int tiles = (key0 + n - 1) / 64 - key0 / 64 + 1;
   hipLaunchKernelGGL(k_tiles_kernel, dim3((unsigned)tiles, (unsigned)H, 1u), dim3(NT), 0, stream,
                      contiguous_keys(k, n), (u32x4*)kt, n, H, (const f32x2*)nullptr, 1, key0, dst_ntile,
-                     (const float*)nullptr, (const float*)nullptr, 0.0f);
+                     (const float*)nullptr, (const float*)nullptr, 0.0f, 1.0f);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(v_tiles_kernel, dim3((unsigned)tiles, (unsigned)H, 1u), dim3(NT), 0, stream,

@@ -27,7 +27,8 @@ __device__ __forceinline__ void rot(float& x, float& y, float c, float s) {
   }
 }
 
-template <bool BF16>
+// INVERSE: rotate by the negated angles (the transpose of the rotation).
+template <bool BF16, bool INVERSE>
 __global__ __launch_bounds__(NT) void rope_kernel(const void* src, void* dst, int64_t n_tok, int T, int H,
                                                   const int32_t* __restrict__ pos, double base) {
   __shared__ f32x2 cs[TOK][32];
@@ -43,7 +44,7 @@ __global__ __launch_bounds__(NT) void rope_kernel(const void* src, void* dst, in
       const double pp = (double)pos[2 * t + axis];
       const double theta = pp * pow(base, -(double)pair / 16.0);
       cv = (float)cos(theta);
-      sv = (float)sin(theta);
+      sv = INVERSE ? -(float)sin(theta) : (float)sin(theta);
     }
     cs[lt][k] = f32x2{cv, sv};
   }
@@ -126,13 +127,17 @@ hipError_t launch_layer_norm_f32(const float* src, float* dst, int64_t n_tok, in
 }
 
 hipError_t launch_rope(const void* src, void* dst, bool bf16, int64_t n_tok, int T, int H, const int32_t* pos_yx,
-                       double base, hipStream_t stream) {
+                       double base, hipStream_t stream, bool inverse) {
   if (n_tok <= 0) return hipSuccess;
   const unsigned blocks = (unsigned)((n_tok + TOK - 1) / TOK);
-  if (bf16)
-    hipLaunchKernelGGL(rope_kernel<true>, dim3(blocks), dim3(NT), 0, stream, src, dst, n_tok, T, H, pos_yx, base);
+  if (bf16 && !inverse)
+    hipLaunchKernelGGL((rope_kernel<true, false>), dim3(blocks), dim3(NT), 0, stream, src, dst, n_tok, T, H, pos_yx, base);
+  else if (bf16)
+    hipLaunchKernelGGL((rope_kernel<true, true>), dim3(blocks), dim3(NT), 0, stream, src, dst, n_tok, T, H, pos_yx, base);
+  else if (!inverse)
+    hipLaunchKernelGGL((rope_kernel<false, false>), dim3(blocks), dim3(NT), 0, stream, src, dst, n_tok, T, H, pos_yx, base);
   else
-    hipLaunchKernelGGL(rope_kernel<false>, dim3(blocks), dim3(NT), 0, stream, src, dst, n_tok, T, H, pos_yx, base);
+    hipLaunchKernelGGL((rope_kernel<false, true>), dim3(blocks), dim3(NT), 0, stream, src, dst, n_tok, T, H, pos_yx, base);
   return hipGetLastError();
 }
 

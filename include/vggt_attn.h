@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define VGGT_ATTN_ABI_VERSION 4
+#define VGGT_ATTN_ABI_VERSION 5
 #define VGGT_HEAD_DIM 64
 
 typedef enum {
@@ -193,6 +193,44 @@ vggt_status vggt_global_attn_ex(const void* q, const void* k, const void* v, voi
                                 const vggt_qk_norm* norm, void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * Training support: the forward pass that also saves each query row's
+ * log-normaliser, and the gradients of frame and global attention (the chain
+ * rule through softmax(Q K^T * scale) V of the slide deck, Section V, slide
+ * 5/10, with RoPE as in vggt_attn_rope; the VGGT-JAX README trains and checks
+ * gradients of this attention).
+ *
+ * vggt_frame_attn_train / vggt_global_attn_train: as vggt_frame_attn /
+ * vggt_global_attn, and lse [S*T, H] float32 (device, written) receives
+ * log(sum_j exp(scale * <q'_i, k'_j>)) of every query row (natural log; q', k'
+ * rotated).  lse must not overlap another buffer (VGGT_ERR_ALIAS).
+ *
+ * vggt_frame_attn_backward / vggt_global_attn_backward: given q, k, v, the
+ * forward output o, its upstream gradient dout (all [S, T, H, 64], dtype dt)
+ * and lse from the training forward, write dq, dk, dv [S, T, H, 64] (dtype
+ * dt): the gradients with respect to the unrotated q and k and to v.  bf16:
+ * products in bf16 on the matrix cores with fp32 accumulation (probabilities
+ * and score gradients rounded to bf16 before their products); fp32: fp32
+ * throughout (debug).  Workspace of vggt_attn_backward_workspace(S, T, H,
+ * global, rope_on, dt) bytes.  The gradients must not overlap any input, lse,
+ * the workspace or each other.  No LayerNorm prologue in the backward.
+ */
+vggt_status vggt_frame_attn_train(const void* q, const void* k, const void* v, void* o, float* lse, vggt_dtype dt,
+                                  int S, int T, int H, const int32_t* pos_yx, float rope_base, float scale,
+                                  void* workspace, size_t ws_bytes, void* stream);
+vggt_status vggt_global_attn_train(const void* q, const void* k, const void* v, void* o, float* lse, vggt_dtype dt,
+                                   int S, int T, int H, const int32_t* pos_yx, float rope_base, float scale,
+                                   int kv_splits, void* workspace, size_t ws_bytes, void* stream);
+size_t vggt_attn_backward_workspace(int S, int T, int H, int global, int rope_on, vggt_dtype dt);
+vggt_status vggt_frame_attn_backward(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                                     const float* lse, void* dq, void* dk, void* dv, vggt_dtype dt, int S, int T,
+                                     int H, const int32_t* pos_yx, float rope_base, float scale, void* workspace,
+                                     size_t ws_bytes, void* stream);
+vggt_status vggt_global_attn_backward(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                                      const float* lse, void* dq, void* dk, void* dv, vggt_dtype dt, int S, int T,
+                                      int H, const int32_t* pos_yx, float rope_base, float scale, void* workspace,
+                                      size_t ws_bytes, void* stream);
+
+/*
  * FlashVGGT descriptor pooling (FlashVGGT README, "Overview": each frame's
  * spatial information is compressed into a compact descriptor set; "Key
  * Arguments": --kv_downfactor, default 4, taken here as a ph x pw = 2 x 2
@@ -283,7 +321,8 @@ vggt_status vggt_descriptor_chunked_xattn(const void* q, const void* cache, void
  * vggt_timer_start(capacity) creates 2*capacity HIP events on the current
  * device and arms the timer: each later attention kernel launch on that
  * device (by vggt_frame_attn, vggt_global_attn, vggt_descriptor_xattn,
- * vggt_descriptor_cache_attn or vggt_descriptor_chunked_xattn), up to
+ * vggt_descriptor_cache_attn or vggt_descriptor_chunked_xattn, their _qknorm,
+ * _ex and _train forms, and the two kernels of the bf16 backward), up to
  * `capacity` of them, is bracketed by two events recorded on the call's
  * stream.  capacity in [1, 2^20]; VGGT_ERR_SHAPE if the timer is already
  * running.
@@ -301,7 +340,9 @@ typedef enum {
   VGGT_TIMER_GLOBAL = 2,
   VGGT_TIMER_XATTN = 3,
   VGGT_TIMER_CACHE = 4,
-  VGGT_TIMER_CHUNKED = 5
+  VGGT_TIMER_CHUNKED = 5,
+  VGGT_TIMER_BWD_DQ = 6,   /* bf16 backward: the dQ kernel */
+  VGGT_TIMER_BWD_DKDV = 7  /* bf16 backward: the dK/dV kernel */
 } vggt_timer_kind;
 vggt_status vggt_timer_start(int capacity);
 vggt_status vggt_timer_stop(float* ms, int* kinds, int n_max, int* n_recorded);

@@ -280,7 +280,8 @@ def attention_backward(q, k, v, dout, *, group_q: int = 0, group_k: int = 0, sca
     """Gradients of multi-head attention (oracle.c, oracle_attention_backward).
     q/dout [nq, H, D], k/v [nk, H, D].  Returns (dq [len(rows) or nq, H, D],
     dk, dv [len(cols) or nk, H, D], lse [nq, H]) in float64; lse is the natural
-    log-normaliser of every query row."""
+    log-normaliser of each query row that the requested gradients read (zero
+    for the other rows)."""
     q64, k64, v64, d64 = (np.ascontiguousarray(to_f64(x), dtype=np.float64) for x in (q, k, v, dout))
     nq, H, D = q64.shape
     nk = k64.shape[0]

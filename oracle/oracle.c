@@ -266,6 +266,7 @@ int oracle_attention(const double* q, const double* k, const double* v, double* 
 typedef struct {
   const double *q, *k, *v, *dout;
   double *dq, *dk, *dv, *lse, *csum;
+  const char* need;  /* pass 1 runs for the query rows that passes 2 and 3 read */
   int64_t nq, nk;
   int H, D;
   int64_t group_q, group_k;
@@ -314,6 +315,7 @@ static void* bwd_worker(void* arg) {
       const double* qi = J->q + i * stride + (int64_t)h * D;
       const double* doi = J->dout + i * stride + (int64_t)h * D;
       if (J->phase == 1) {
+        if (!J->need[i]) continue;
         double m = -INFINITY;
         for (int64_t j = 0; j < nk; ++j) {
           sc[j] = J->scale * dot(qi, J->k + (k0 + j) * stride + (int64_t)h * D, D);
@@ -384,7 +386,18 @@ int oracle_attention_backward(const double* q, const double* k, const double* v,
   } else {
     ncols = nk;
   }
+  /* rows whose log-normaliser is read: the requested query rows, and every query
+     whose key set holds a requested key */
+  char* need = (char*)calloc((size_t)nq, 1);
+  for (int64_t i = 0; i < nrows; ++i) need[rows ? rows[i] : i] = 1;
+  for (int64_t c = 0; c < ncols; ++c) {
+    const int64_t j = cols ? cols[c] : c;
+    const int64_t i0 = group_q > 0 ? (j / group_k) * group_q : 0;
+    const int64_t i1 = group_q > 0 ? i0 + group_q : nq;
+    for (int64_t i = i0; i < i1; ++i) need[i] = 1;
+  }
   bwd_job J;
+  J.need = need;
   J.q = q; J.k = k; J.v = v; J.dout = dout;
   J.dq = dq; J.dk = dk; J.dv = dv;
   J.lse = lse;  /* [nq][H], filled by pass 1 */
@@ -404,6 +417,7 @@ int oracle_attention_backward(const double* q, const double* k, const double* v,
   }
   pthread_mutex_destroy(&J.lock);
   free(J.csum);
+  free(need);
   return 0;
 }
 

@@ -32,7 +32,7 @@ def L():
 
 def test_exports_match_header(L):
     declared = header_functions()
-    assert len(declared) == 25
+    assert len(declared) == 30
     out = subprocess.run(["nm", "-D", "--defined-only", ffv.LIB_PATH], capture_output=True, text=True,
                          check=True).stdout
     exported = sorted(set(m for m in re.findall(r"\bT (vggt_\w+)", out)))
@@ -41,7 +41,7 @@ def test_exports_match_header(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.vggt_abi_version() == 4
+    assert L.vggt_abi_version() == 5
     for code, name in ffv.STATUS.items():
         assert L.vggt_status_str(code).decode() == name
     assert L.vggt_status_str(99).decode() == "VGGT_ERR_UNKNOWN"
@@ -228,3 +228,34 @@ def test_omega_variant_arguments(L):
     f = L.vggt_frame_attn_ex
     assert f(_p(A), _p(B), _p(C), _p(O), 0, 2, 8, 0, 1, None, 100.0, 0.0, None, None, 0, None) == SHAPE
     assert f(_p(A), _p(B), _p(C), _p(O), 0, 2, 8, 6, 1, None, 100.0, 0.0, None, None, 0, None) == WS
+
+
+def test_backward_arguments(L):
+    BF16, F32 = 0, 1
+    S, T, H = 4, 100, 2
+    n, tiles = S * T, (S * T + 63) // 64
+    # bf16 global: seven tile sets plus two statistics rows per head; RoPE adds the table and rotated copies
+    base = L.vggt_attn_backward_workspace(S, T, H, 1, 0, BF16)
+    assert base >= 7 * H * tiles * 64 * 64 * 2 + 2 * H * tiles * 64 * 4
+    assert L.vggt_attn_backward_workspace(S, T, H, 1, 1, BF16) >= base + 2 * n * H * 64 * 2
+    assert L.vggt_attn_backward_workspace(S, T, H, 0, 0, BF16) >= 7 * S * H * 2 * 64 * 64 * 2
+    assert L.vggt_attn_backward_workspace(S, T, H, 1, 1, F32) >= 4 * n * H * 64 * 4
+    assert L.vggt_attn_backward_workspace(S, 0, H, 1, 0, BF16) == 0
+    b = L.vggt_global_attn_backward
+    Q, K, V, Ot, DO, LS, DQ, DK, DV, WSP = (0x1000000 * (i + 1) for i in range(10))
+    big = 1 << 24
+    args = lambda **kw: [_p(kw.get(n, d)) if d is not None else None for n, d in
+                         (("q", Q), ("k", K), ("v", V), ("o", Ot), ("do", DO), ("lse", LS), ("dq", DQ), ("dk", DK),
+                          ("dv", DV))]
+    tail = [0, 2, 8, 1, None, 100.0, 0.0, _p(WSP), big, None]
+    assert b(*args(lse=None), *tail) == NULL
+    assert b(*args(dq=Q), *tail) == ALIAS             # dq is q
+    assert b(*args(dk=DQ), *tail) == ALIAS            # dk is dq
+    assert b(*args(dv=LS), *tail) == ALIAS            # dv is lse
+    assert b(*args(lse=LS + 2), *tail) == ALIGN
+    assert b(*args(), 0, 2, 8, 1, None, 100.0, 0.0, _p(WSP), 16, None) == WS
+    assert b(*args(), 0, 2, 0, 1, None, 100.0, 0.0, _p(WSP), big, None) == SHAPE
+    t = L.vggt_global_attn_train
+    assert t(_p(A), _p(B), _p(C), _p(O), None, 0, 2, 8, 1, None, 100.0, 0.0, 0, _p(0x10000000), big, None) == NULL
+    assert t(_p(A), _p(B), _p(C), _p(O), _p(A + 64), 0, 2, 8, 1, None, 100.0, 0.0, 0, _p(0x10000000), big,
+             None) == ALIAS
