@@ -60,9 +60,20 @@ namespace {
 constexpr int D = kHeadDim;
 constexpr int BK = kAttnKeyTile;  // 64 keys per tile
 constexpr int NW = 4;             // waves per workgroup
+#ifndef VGGT_ATTN_QB
+#define VGGT_ATTN_QB 2
+#endif
+#ifndef VGGT_ATTN_NSTAGE
+#define VGGT_ATTN_NSTAGE 4
+#endif
+#ifndef VGGT_ATTN_WPE
+#define VGGT_ATTN_WPE 2
+#endif
 constexpr int NT = NW * 64;
-constexpr int BQ = NW * 64;       // 64 queries per wave
-constexpr int NSTAGE = 4;         // LDS ring depth (tiles in flight = NSTAGE - 1)
+constexpr int QB = VGGT_ATTN_QB;  // 32-query MFMA column blocks per wave
+constexpr int BQ = NW * 32 * QB;  // queries per workgroup
+constexpr int NSTAGE = VGGT_ATTN_NSTAGE;  // LDS ring depth (tiles in flight = NSTAGE - 1)
+static_assert(QB == 1 || QB == 2, "one or two query blocks per wave");
 constexpr float kSumLimit = 18446744073709551616.0f;  // 2^64
 constexpr float kRaise = 32.0f;   // move m when a tile max exceeds it by this
 constexpr float kLow = -64.0f;    // first tile: move m down when the max is below this
@@ -103,7 +114,7 @@ struct Tile {
   f32x16 s[2][2];  // [kb][qb]
 };
 
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(VGGT_ATTN_WPE, VGGT_ATTN_WPE)))
 void attn_fwd_bf16_kernel(AttnProblem p) {
   __shared__ Smem sm;
   const int tid = threadIdx.x;
@@ -147,7 +158,7 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
   const int kend = min(nk_seq, kbeg + p.keys_per_split);
   const int ntiles = (kend - kbeg + BK - 1) / BK;
 
-  const int q0 = qt * BQ + wave * 64;  // first query of this wave
+  const int q0 = qt * BQ + wave * 32 * QB;  // first query of this wave
   const bool active = q0 < nq_seq;
 
   // ---- tile loads: each wave copies two 1 KiB blocks of the K tile and two of the V^T tile
@@ -169,11 +180,11 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
   // ---- Q fragments (B operand of S^T = K Q^T): lane holds query q0+32*qb+l32,
   //      dims 16*dc + 8*hi .. +7 (the other 32 dims sit in lane ^ 32), after an
   //      optional per-head LayerNorm, rotated and scaled by scale*log2(e).
-  bf16x8 qf[2][4];
+  bf16x8 qf[QB][4];
   {
     const f32x2* __restrict__ tab = p.rope_tab;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
       const int qi = q0 + 32 * qb + l32;
       const bool ok = qi < nq_seq;
       const int qrow = ok ? qi : 0;
@@ -239,20 +250,21 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
   }
 
   // ---- running state
-  f32x16 o[2][2];  // [db][qb]: O^T rows 32*db + 8*(r/4) + 4*hi + r%4, column = query
+  f32x16 o[2][QB];  // [db][qb]: O^T rows 32*db + 8*(r/4) + 4*hi + r%4, column = query
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < QB; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[a][b][r] = 0.0f;
-  float mref[2] = {0.0f, 0.0f};  // log2 units
-  float lsum[2] = {0.0f, 0.0f};  // this lane's partial row sums
-  f32x16 negm[2];                // -m of the lane's query, replicated: accumulator input of S^T
+  float mref[QB], lsum[QB];  // reference (log2 units) and this lane's partial row sums
+  f32x16 negm[QB];           // -m of the lane's query, replicated: accumulator input of S^T
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
+  for (int qb = 0; qb < QB; ++qb) {
+    mref[qb] = lsum[qb] = 0.0f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) negm[qb][r] = 0.0f;
+  }
 
   f32x16 s0[2], s1[2];       // [kb] scores of query blocks 0 and 1
   u32x4 p0[2][2], p1[2][2];  // [kb][j] bf16 pairs of keys 32kb+16j+8hi+0..7 (B operand of P V)
@@ -383,19 +395,27 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
     read_k(stage);
     qk(s0, 0);
     if constexpr (masked) mask(s0, kbeg + t * BK);
-    qk(s1, 1);
-    float ls0 = soft(s0, false, 0.0f, p0);
-    VGGT_INTERLEAVE(8, 8);
-    if constexpr (masked) mask(s1, kbeg + t * BK);
-    if (first || __any(!(ls0 <= kSumLimit))) ls0 = slow(s0, 0, first, p0);
-    lsum[0] += ls0;
-    read_v(stage);
-    pv(p0, 0);
-    float ls1 = soft(s1, false, 0.0f, p1);
-    VGGT_INTERLEAVE(8, 8);
-    if (first || __any(!(ls1 <= kSumLimit))) ls1 = slow(s1, 1, first, p1);
-    lsum[1] += ls1;
-    pv(p1, 1);
+    if constexpr (QB == 2) {
+      qk(s1, 1);
+      float ls0 = soft(s0, false, 0.0f, p0);
+      VGGT_INTERLEAVE(8, 8);
+      if constexpr (masked) mask(s1, kbeg + t * BK);
+      if (first || __any(!(ls0 <= kSumLimit))) ls0 = slow(s0, 0, first, p0);
+      lsum[0] += ls0;
+      read_v(stage);
+      pv(p0, 0);
+      float ls1 = soft(s1, false, 0.0f, p1);
+      VGGT_INTERLEAVE(8, 8);
+      if (first || __any(!(ls1 <= kSumLimit))) ls1 = slow(s1, QB - 1, first, p1);
+      lsum[QB - 1] += ls1;
+      pv(p1, QB - 1);
+    } else {
+      float ls0 = soft(s0, false, 0.0f, p0);
+      if (first || __any(!(ls0 <= kSumLimit))) ls0 = slow(s0, 0, first, p0);
+      lsum[0] += ls0;
+      read_v(stage);
+      pv(p0, 0);
+    }
   };
   using yes = std::true_type;
   using no = std::false_type;
@@ -426,7 +446,7 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
 
   // ---- epilogue
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     const float ltot = lsum[qb] + __shfl_xor(lsum[qb], 32);
     const int qi = q0 + 32 * qb + l32;
     if (qi >= nq_seq) continue;

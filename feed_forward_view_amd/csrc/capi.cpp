@@ -33,7 +33,10 @@ constexpr int kMaxHeads = 128;
 constexpr int64_t kMaxTokens = int64_t(1) << 28;
 constexpr int kMaxSplits = 64;
 constexpr int kAssumedCUs = 256;       // MI355X; used only to size the key split
-constexpr int kWorkgroupsPerCU = 2;  // the bf16 kernel runs two 4-wave workgroups per CU
+#ifndef VGGT_ATTN_WPE
+#define VGGT_ATTN_WPE 2
+#endif
+constexpr int kWorkgroupsPerCU = VGGT_ATTN_WPE;  // the bf16 kernel's 4-wave workgroups resident per CU
 
 // ---- device check, cached per device (read-only after first use)
 struct DevInfo {

@@ -32,7 +32,8 @@ __global__ __launch_bounds__(NT) void rope_table_kernel(const int32_t* __restric
 // Row of key j of sequence sq in src.main (>= 0), or -1 - (row in src.extra).
 __device__ __forceinline__ int64_t key_row(const KeySrc& src, int sq, int64_t j) {
   if (j >= src.n_main) return -1 - (j - src.n_main);
-  const int64_t r = src.frame_len > 0 ? (j / src.frame_len) * src.frame_stride + j % src.frame_len : j;
+  // keys stay below 2^28 (host check): 32-bit division
+  const int64_t r = src.frame_len > 0 ? (int64_t)((int)j / src.frame_len) * src.frame_stride + (int)j % src.frame_len : j;
   return (int64_t)sq * src.seq_rows + r;
 }
 
@@ -103,14 +104,21 @@ __global__ __launch_bounds__(NT) void k_tiles_kernel(KeySrc k, u32x4* __restrict
           for (int j = 0; j < 8; ++j) f[j] = __builtin_fmaf((f[j] - mu) * inv, ln_g[8 * u + j], ln_b[8 * u + j]);
         }
         if (table && row >= 0) {
-          const int t = (int)(row % rope_T);
+          // rows stay below 2^28 (host check), so the position is taken in 32 bits
+          const int t = (int)row % rope_T;
+          const f32x4* tq = (const f32x4*)(table + t * 32 + 4 * u);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const f32x2 cs = table[t * 32 + 4 * u + e];
-            if (cs[1] != 0.0f) {
-              const float x = f[2 * e], y = f[2 * e + 1];
-              f[2 * e] = __builtin_fmaf(x, cs[0], -y * cs[1]);
-              f[2 * e + 1] = __builtin_fmaf(x, cs[1], y * cs[0]);
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const f32x4 cs2 = tq[h2];  // (cos, sin) of pairs 4u + 2h2 and 4u + 2h2 + 1
+#pragma unroll
+            for (int e2 = 0; e2 < 2; ++e2) {
+              const int e = 2 * h2 + e2;
+              const float c = cs2[2 * e2], sn = cs2[2 * e2 + 1];
+              if (sn != 0.0f) {
+                const float x = f[2 * e], y = f[2 * e + 1];
+                f[2 * e] = __builtin_fmaf(x, c, -y * sn);
+                f[2 * e + 1] = __builtin_fmaf(x, sn, y * c);
+              }
             }
           }
         }

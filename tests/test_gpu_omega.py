@@ -98,10 +98,10 @@ def test_omega_full_size():
     n = S * Ta
     rows = sample_rows(n, Ta, S, seed=wl.index + 11, n_random=48)
     ref = oracle.global_attn_ex(q, k, v, S, T, Ta, xq, xk, xv, pos=pos, rows=np.concatenate([rows, n + np.arange(E)]))
-    got = to_f64(go)[:, :Ta].reshape(n, H, 64)[rows]
+    got = to_f64(go[:, :Ta].contiguous()).reshape(n, H, 64)[rows]
     check_bf16(got, ref[:rows.size], f"s64 global_ex frames ({rows.size} rows)")
     check_bf16(to_f64(xo), ref[rows.size:], "s64 global_ex extras")
     del go
     fo = ffv.vggt_frame_attn_ex(qd, kd, vd, Ta, pos_yx=pd)
     fr = oracle.frame_attn(q[:, :Ta], k[:, :Ta], v[:, :Ta], S, Ta, pos=pos[:Ta], rows=rows)
-    check_bf16(to_f64(fo)[:, :Ta].reshape(n, H, 64)[rows], fr, f"s64 frame_ex ({rows.size} rows)")
+    check_bf16(to_f64(fo[:, :Ta].contiguous()).reshape(n, H, 64)[rows], fr, f"s64 frame_ex ({rows.size} rows)")
