@@ -28,7 +28,7 @@
 // 16-byte slot.  The query operand of the scores carries scale*log2(e) and is
 // rounded exactly as in the forward kernel, so the recomputed probabilities
 // match the saved log-normaliser.  Rows past the end are zero in every tile
-// and their lse2 is +inf, so they contribute nothing.
+// and their -lse2 is -inf, so they contribute nothing.
 #include "common.h"
 
 namespace vggt {
@@ -146,8 +146,8 @@ void attn_bwd_dq_kernel(AttnBwdProblem p) {
     qf[dc] = as_bf16x8(r);
     df[dc] = as_bf16x8(g);
   }
-  const f32x16 nl = splat(ok ? -p.lse2[sbase + qi] : -INFINITY);
-  const f32x16 nd = splat(ok ? -p.dsum[sbase + qi] : 0.0f);
+  const f32x16 nl = splat(ok ? p.lse2[sbase + qi] : -INFINITY);
+  const f32x16 nd = splat(ok ? p.dsum[sbase + qi] : 0.0f);
 
   f32x16 acc[2] = {splat(0.0f), splat(0.0f)};  // dQ^T [db]: dims 32db + ..., this lane's query
   for (int t = 0; t < p.ntile; ++t) {
@@ -295,10 +295,10 @@ void attn_bwd_dkdv_kernel(AttnBwdProblem p) {
         const f32x4 d0 = *(const f32x4*)&sm.st[stage][1][q0], d1 = *(const f32x4*)&sm.st[stage][1][q0 + 4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          s[8 * h8 + e] = -l0[e];
-          s[8 * h8 + 4 + e] = -l1[e];
-          dp[8 * h8 + e] = -d0[e];
-          dp[8 * h8 + 4 + e] = -d1[e];
+          s[8 * h8 + e] = l0[e];
+          s[8 * h8 + 4 + e] = l1[e];
+          dp[8 * h8 + e] = d0[e];
+          dp[8 * h8 + 4 + e] = d1[e];
         }
       }
       const int row = 32 * qb + l32;
@@ -351,7 +351,8 @@ void attn_bwd_dkdv_kernel(AttnBwdProblem p) {
 // Pre-pass and fp32 debug kernels
 // ---------------------------------------------------------------------------
 
-// lse2 = lse * log2(e) and D = rowsum(dO * O) per (sequence, head, row), rows padded to ntile*64.
+// -lse * log2(e) and -rowsum(dO * O) per (sequence, head, row), rows padded to ntile*64 with
+// (-inf, 0); stored negated because both enter the products as accumulator inputs.
 template <bool BF16>
 __global__ __launch_bounds__(NT) void bwd_pre_kernel(const void* o, const void* dout, const float* __restrict__ lse,
                                                      float* __restrict__ lse2, float* __restrict__ dsum, int nseq,
@@ -362,7 +363,7 @@ __global__ __launch_bounds__(NT) void bwd_pre_kernel(const void* o, const void* 
   const int h = (int)((i / npad) % H);
   const int sq = (int)(i / ((int64_t)npad * H));
   if (r >= n) {
-    lse2[i] = INFINITY;
+    lse2[i] = -INFINITY;
     dsum[i] = 0.0f;
     return;
   }
@@ -389,8 +390,8 @@ __global__ __launch_bounds__(NT) void bwd_pre_kernel(const void* o, const void* 
       for (int e = 0; e < 4; ++e) acc = __builtin_fmaf(a[e], b[e], acc);
     }
   }
-  lse2[i] = lse[tok * H + h] * kLog2e;
-  dsum[i] = acc;
+  lse2[i] = -lse[tok * H + h] * kLog2e;
+  dsum[i] = -acc;
 }
 
 // fp32: one thread per (sequence, row, head).  DQ: row = query, loop over keys;
@@ -428,8 +429,8 @@ __global__ __launch_bounds__(NT) void attn_bwd_f32_kernel(const float* __restric
       sdot = __builtin_fmaf(a[d], oa[d], sdot);
       pdot = __builtin_fmaf(b[d], ob[d], pdot);
     }
-    const float pr = __builtin_amdgcn_exp2f(sdot * c - lse2[sb + qrow]);
-    const float ds = pr * (pdot - dsum[sb + qrow]);
+    const float pr = __builtin_amdgcn_exp2f(sdot * c + lse2[sb + qrow]);  // lse2, dsum hold the negated values
+    const float ds = pr * (pdot + dsum[sb + qrow]);
     for (int d = 0; d < D; ++d) {
       x[d] = __builtin_fmaf(ds, oa[d], x[d]);        // dq += ds k_j  |  dk += ds q_i
       if (!DQ) y[d] = __builtin_fmaf(pr, ob[d], y[d]);  // dv += p dO_i

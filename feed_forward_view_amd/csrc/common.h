@@ -92,8 +92,8 @@ struct AttnBwdProblem {
   const void* do_rows;     // dO, row tiles
   const void* q_trans;     // Q rotated, transposed tiles
   const void* do_trans;    // dO, transposed tiles
-  const float* lse2;       // [nseq][H][ntile*64]: log2-normaliser of each query row (+inf past the end)
-  const float* dsum;       // [nseq][H][ntile*64]: rowsum(dO * O) (0 past the end)
+  const float* lse2;       // [nseq][H][ntile*64]: minus the log2-normaliser of each query row (-inf past the end)
+  const float* dsum;       // [nseq][H][ntile*64]: minus rowsum(dO * O) (0 past the end)
   void* dq;                // [tokens][H][64] bf16 outputs
   void* dk;
   void* dv;
@@ -106,8 +106,8 @@ struct AttnBwdProblem {
 
 // dq: the dQ kernel, else the dK/dV kernel.
 hipError_t launch_attn_bwd_bf16(const AttnBwdProblem& p, bool dq, hipStream_t stream);
-// lse2 / dsum of the backward pass from the forward's lse and rowsum(dO * O);
-// rows [nseq][H][ntile*64] padded with (+inf, 0).
+// Negated lse2 / dsum of the backward pass from the forward's lse and rowsum(dO * O);
+// rows [nseq][H][ntile*64] padded with (-inf, 0).
 hipError_t launch_attn_bwd_pre(const void* o, const void* dout, bool bf16, const float* lse, float* lse2,
                                float* dsum, int nseq, int n, int64_t seq_stride, int H, int ntile,
                                hipStream_t stream);
