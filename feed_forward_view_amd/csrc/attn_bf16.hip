@@ -23,12 +23,13 @@
 // the key index swapped) so that the S^T accumulator registers are, in order,
 // exactly the bf16 B operand of the P V product.
 //
-// Overlap.  On gfx950 the exponentials (transcendental unit) can issue
-// while an MFMA of the same SIMD executes, but ordinary vector ALU work
-// cannot, so the loop keeps non-exponential VALU work per tile to the
-// minimum (one cvt and one dot2 per score pair) and interleaves each query
-// block's exponentials with the other block's MFMAs; two waves per SIMD
-// supply the rest of the overlap.
+// Overlap.  On gfx950 a wave's own VALU instructions do not overlap its
+// MFMAs; VALU work of the other wave on the SIMD can: plain VALU (fma, add,
+// cvt) hides completely behind a running MFMA, exponentials mostly, dot2
+// not at all.  With two waves per SIMD that both mix the two kinds about a
+// third of the VALU time hides, so the loop keeps VALU work per tile to the
+// minimum (one exp per score, one cvt and one dot2 per score pair) and
+// interleaves each query block's exponentials with the other block's MFMAs.
 //
 // Softmax reference.  m starts at 0 and stays there while a row's scores stay
 // within 2^32 of it.  The first tile, and any tile whose partial row sum
