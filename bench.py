@@ -225,6 +225,8 @@ def main() -> int:
 
     if not args.no_extras:
         result["qknorm"] = bench_qknorm(ffv, qd, kd, vd, posd, ws_g, ws_f, max(3, args.steps // 2), flops)
+    if not args.no_extras:
+        result["configs"] = bench_configs(ffv, dev, max(3, args.steps // 2), qd)
     if not (args.no_stream or args.no_extras):
         result["stream"] = bench_stream(ffv, dev, max(3, args.steps // 2), 2)
     if not (args.no_backward or args.no_extras):
@@ -236,6 +238,92 @@ def main() -> int:
                                                                        args.cpu_row_stride)
     print(json.dumps(result), flush=True)
     return 0
+
+
+_FLUSH = None
+
+
+def _flush_cache():
+    """Overwrite 1 GiB of device memory so that the 256 MB Infinity Cache holds none of
+    the next call's inputs (HBM-bound measurements)."""
+    import torch
+
+    global _FLUSH
+    if _FLUSH is None:
+        _FLUSH = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    _FLUSH.fill_(1.0)
+
+
+def _median_ms(fn, iters, warm=2, flush=False):
+    """Median duration of fn() from HIP events on the current stream (optionally with the
+    cache overwritten before each timed call, outside the timed interval)."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    for _ in range(warm):
+        fn()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        if flush:
+            _flush_cache()
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) for a, b in ev]))
+
+
+def bench_configs(ffv, dev, iters, qd):
+    """The smaller workloads (4 frames at 224x224: N=1044; 8 frames at 518x518: N=10992):
+    frame and global attention with RoPE, kernel times from the library timer; and the
+    standalone in-place RoPE pass on the S=32 Q tensor next to a plain device copy of the
+    same bytes."""
+    import torch
+
+    import workload
+
+    out = {}
+    for name in ("vggt-224-s4", "vggt-518-s8"):
+        wl = workload.WORKLOADS[name]
+        S, T, H, N = wl.S, wl.T, wl.H, wl.N
+        q, k, v = (torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16) for a in wl.qkv_bf16())
+        pos = torch.from_numpy(wl.positions()).to(dev)
+        o = torch.empty_like(q)
+        ws_f = torch.empty(max(1, ffv.vggt_frame_attn_workspace(S, T, H, True)), dtype=torch.uint8, device=dev)
+        ws_g = torch.empty(max(1, ffv.vggt_global_attn_workspace(S, T, H, 0, True)), dtype=torch.uint8, device=dev)
+        res = {"S": S, "T": T, "N": N}
+        for kind, fn, fl in (
+                ("frame", lambda: ffv.vggt_frame_attn(q, k, v, out=o, pos_yx=pos, workspace=ws_f), attn_flops(T, T, H) * S),
+                ("global", lambda: ffv.vggt_global_attn(q, k, v, out=o, pos_yx=pos, workspace=ws_g), attn_flops(N, N, H))):
+            fn()
+            torch.cuda.synchronize()
+            ffv.vggt_timer_start(iters)
+            call_ms = _median_ms(fn, iters, warm=0)
+            kern = float(np.mean([ms for _, ms in ffv.vggt_timer_stop()]))
+            res[f"{kind}_call_ms"] = round(call_ms, 4)
+            res[f"{kind}_kernel_ms"] = round(kern, 4)
+            res[f"{kind}_kernel_tflops"] = round(fl / (kern * 1e-3) / 1e12, 2)
+            res[f"{kind}_kernel_frac_of_bf16_peak"] = round(fl / (kern * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+        res["ms_per_layer"] = round(res["frame_call_ms"] + res["global_call_ms"], 4)
+        out[name] = res
+    # standalone RoPE: read + write every Q element once
+    wl = workload.WORKLOADS["vggt-518-s32"]
+    x = qd.clone()
+    pos = torch.from_numpy(wl.positions()).to(dev)
+    rope_ms = _median_ms(lambda: ffv.vggt_attn_rope(x, pos), iters, flush=True)
+    y = torch.empty_like(x)
+    copy_ms = _median_ms(lambda: y.copy_(x), iters, flush=True)
+    nbytes = 2 * x.numel() * x.element_size()
+    out["rope_standalone"] = {
+        "workload": f"vggt_attn_rope in place on Q of {wl.name} ({x.numel() * 2 / 1e6:.1f} MB read and written); "
+                    f"1 GiB overwritten before each timed call so the inputs come from HBM",
+        "ms": round(rope_ms, 4),
+        "gbs": round(nbytes / (rope_ms * 1e-3) / 1e9, 1),
+        "frac_of_hbm_peak": round(nbytes / (rope_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "device_copy_gbs": round(nbytes / (copy_ms * 1e-3) / 1e9, 1),
+    }
+    return out
 
 
 def bench_qknorm(ffv, qd, kd, vd, posd, ws_g, ws_f, iters, flops):
@@ -355,12 +443,15 @@ def bench_omega(ffv, dev, iters):
     ws_e = torch.empty(max(1, int(ffv.lib().vggt_global_attn_ex_workspace(S, T, Ta, E, H, 0, ffv.PRE_ROPE, 0))),
                        dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
+    ws_f = torch.empty(max(1, ffv.vggt_frame_attn_workspace(S, T, H, True)), dtype=torch.uint8, device=dev)
     calls = {
+        "frame": lambda: ffv.vggt_frame_attn(qd, kd, vd, out=out, pos_yx=pd, workspace=ws_f),
         "global": lambda: ffv.vggt_global_attn(qd, kd, vd, out=out, pos_yx=pd, workspace=ws_g),
         "global_ex": lambda: ffv.vggt_global_attn_ex(qd, kd, vd, Ta, *x, out=out, xout=xo, pos_yx=pd,
                                                      workspace=ws_e),
     }
-    flops = {"global": attn_flops(S * T, S * T, H), "global_ex": attn_flops(S * Ta + E, S * Ta + E, H)}
+    flops = {"frame": attn_flops(T, T, H) * S, "global": attn_flops(S * T, S * T, H),
+             "global_ex": attn_flops(S * Ta + E, S * Ta + E, H)}
     res = {"workload": f"{wl.name}: S={S} frames x T={T} (32x32 patches + 16 registers), H={H}, d=64, RoPE base "
                        f"100; global_ex = {Ta} patch tokens per frame + {E} extra tokens"}
     for name, fn in calls.items():
@@ -380,6 +471,7 @@ def bench_omega(ffv, dev, iters):
         res[f"{name}_kernel_ms"] = round(kernel_ms, 4)
         res[f"{name}_kernel_tflops"] = round(flops[name] / (kernel_ms * 1e-3) / 1e12, 2)
         res[f"{name}_kernel_frac_of_bf16_peak"] = round(flops[name] / (kernel_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+    res["ms_per_layer"] = round(res["frame_call_ms"] + res["global_call_ms"], 4)
     return res
 
 
@@ -441,6 +533,20 @@ def bench_stream(ffv, dev, passes, warmup, chunk_frames=10):
         kern.setdefault(kind, []).append(ms)
     pass_ms = float(np.median([a.elapsed_time(b) for a, b in ev[0::2]]))
     chunked_ms = float(np.median([a.elapsed_time(b) for a, b in ev[1::2]]))
+
+    # the single-forward form of the same workload: pool every frame, then all 137400 queries
+    # against all 36600 descriptors
+    kall = torch.empty((S, Dn, H, 64), dtype=torch.bfloat16, device=dev)
+    vall = torch.empty_like(kall)
+    ws_x = torch.empty(max(1, ffv.vggt_descriptor_xattn_workspace(S, T, Dn, H, 0)), dtype=torch.uint8, device=dev)
+    pool_ms = _median_ms(lambda: ffv.vggt_descriptor_pool(kd, vd, wl.gh, wl.gw, wl.patch_begin, ph, pw, kd=kall,
+                                                          vd=vall), passes, flush=True)
+    ffv.vggt_timer_start(passes)
+    xattn_ms = _median_ms(lambda: ffv.vggt_descriptor_xattn(qd, kall, vall, out=out, workspace=ws_x), passes,
+                          warm=0)
+    xk = [ms for _, ms in ffv.vggt_timer_stop()]
+    x_flops = attn_flops(S * T, S * Dn, H)
+    pool_bytes = 2 * S * T * H * 64 * 2 + 2 * S * Dn * H * 64 * 2
     flops = sum(attn_flops(min(F, S - c * F) * T, min(S, (c + 1) * F) * Dn, H) for c in range(nch))
     cache_kernel_ms = float(np.sum(kern["cache"])) / passes
     chunked_kernel_ms = float(np.mean(kern["chunked"]))
@@ -455,6 +561,16 @@ def bench_stream(ffv, dev, passes, warmup, chunk_frames=10):
         "chunked_one_launch_tflops": round(flops / (chunked_ms * 1e-3) / 1e12, 2),
         "chunked_kernel_ms": round(chunked_kernel_ms, 4),
         "chunked_kernel_frac_of_bf16_peak": round(flops / (chunked_kernel_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "single_forward": {
+            "pool_ms": round(pool_ms, 4),
+            "pool_gbs": round(pool_bytes / (pool_ms * 1e-3) / 1e9, 1),
+            "pool_frac_of_hbm_peak": round(pool_bytes / (pool_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "xattn_tflop": round(x_flops / 1e12, 3),
+            "xattn_call_ms": round(xattn_ms, 4),
+            "xattn_kernel_ms": round(float(np.mean(xk)), 4),
+            "xattn_kernel_tflops": round(x_flops / (float(np.mean(xk)) * 1e-3) / 1e12, 2),
+            "xattn_kernel_frac_of_bf16_peak": round(x_flops / (float(np.mean(xk)) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        },
     }
 
 
