@@ -38,8 +38,8 @@ PEAK_HBM_GBS = 8000.0
 # plain 1 GiB copy (profiles/attn_fwd_bf16_vggt-518-s32_counters.md).  Valid
 # only for the kernel source it was measured on.
 PROFILED_TRAFFIC = {
-    "kernel_source_sha256": "c07bfc7c40dbf28d614702e5894d5367bf48343502341ef15c6a036df2f5c86e",
-    "read_bytes": 1330.7e6,
+    "kernel_source_sha256": "67953bfe1bd2c7c9e6c04b82598265da57cd0aaa18c00f9021a4fcd5cb04de58",
+    "read_bytes": 1331.7e6,
     "write_bytes": 405.2e6,
 }
 
@@ -244,19 +244,20 @@ _FLUSH = None
 
 
 def _flush_cache():
-    """Overwrite 1 GiB of device memory so that the 256 MB Infinity Cache holds none of
-    the next call's inputs (HBM-bound measurements)."""
+    """Read 1 GiB of device memory so that the 256 MB Infinity Cache holds none of the next
+    call's inputs (HBM-bound measurements); a read leaves clean lines, so no write-back of
+    the flush lands inside the timed call."""
     import torch
 
     global _FLUSH
     if _FLUSH is None:
-        _FLUSH = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
-    _FLUSH.fill_(1.0)
+        _FLUSH = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    _FLUSH.sum()
 
 
 def _median_ms(fn, iters, warm=2, flush=False):
     """Median duration of fn() from HIP events on the current stream (optionally with the
-    cache overwritten before each timed call, outside the timed interval)."""
+    cache flushed before each timed call, outside the timed interval)."""
     import torch
 
     stream = torch.cuda.current_stream()
@@ -317,7 +318,7 @@ def bench_configs(ffv, dev, iters, qd):
     nbytes = 2 * x.numel() * x.element_size()
     out["rope_standalone"] = {
         "workload": f"vggt_attn_rope in place on Q of {wl.name} ({x.numel() * 2 / 1e6:.1f} MB read and written); "
-                    f"1 GiB overwritten before each timed call so the inputs come from HBM",
+                    f"1 GiB read before each timed call so the inputs come from HBM",
         "ms": round(rope_ms, 4),
         "gbs": round(nbytes / (rope_ms * 1e-3) / 1e9, 1),
         "frac_of_hbm_peak": round(nbytes / (rope_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
