@@ -81,12 +81,11 @@ constexpr float kLow = -64.0f;    // first tile: move m down when the max is bel
 constexpr float kLn2 = 0.693147180559945309f;
 
 __device__ __forceinline__ int rho(int i) { return (i & ~0xC) | ((i & 4) << 1) | ((i & 8) >> 1); }
-__device__ __forceinline__ int vt_swz(int d) { return (d ^ (d >> 3)) & 7; }
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// K tile:   row r holds key rho(r) of the tile, 8 units of 8 dims; unit u at slot u ^ (r & 7).
-// V^T tile: row d holds channel d of the 64 keys; unit u (keys 8u..8u+7) at slot u ^ vt_swz(d).
+// K tile:   row r holds key rho(r) of the tile, 8 units of 8 dims; unit u at slot u ^ row_swz(r).
+// V^T tile: row d holds channel d of the 64 keys; unit u (keys 8u..8u+7) at slot u ^ col_swz(d).
 struct Smem {
   u32x4 k[NSTAGE][BK][8];
   u32x4 vt[NSTAGE][D][8];
@@ -279,7 +278,7 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
 #pragma unroll
       for (int dc = 0; dc < 4; ++dc) {
         const int u = 2 * dc + hi;
-        kf[kb][dc] = __builtin_bit_cast(bf16x8, sm.k[stage][row][u ^ (row & 7)]);
+        kf[kb][dc] = __builtin_bit_cast(bf16x8, sm.k[stage][row][u ^ row_swz(row)]);
       }
     }
   };
@@ -292,7 +291,7 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
 #pragma unroll
         for (int db = 0; db < 2; ++db) {
           const int d = 32 * db + l32;
-          vf[kb][j][db] = __builtin_bit_cast(bf16x8, sm.vt[stage][d][u ^ vt_swz(d)]);
+          vf[kb][j][db] = __builtin_bit_cast(bf16x8, sm.vt[stage][d][u ^ col_swz(d)]);
         }
       }
   };

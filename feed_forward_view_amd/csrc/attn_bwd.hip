@@ -41,7 +41,6 @@ constexpr int BW = 32;       // queries (dQ) or keys (dK/dV) per wave
 constexpr int BWG = NW * BW;  // per workgroup
 constexpr float kLog2e = 1.44269504088896340736f;
 
-__device__ __forceinline__ int vt_swz(int d) { return (d ^ (d >> 3)) & 7; }
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -168,7 +167,7 @@ void attn_bwd_dq_kernel(AttnBwdProblem p) {
       dp[kb] = nd;
 #pragma unroll
       for (int dc = 0; dc < 4; ++dc) {
-        const int slot = (2 * dc + hi) ^ (row & 7);
+        const int slot = (2 * dc + hi) ^ row_swz(row);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(sm.k[stage][row][slot]), qf[dc], s[kb], 0, 0, 0);
         dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(sm.v[stage][row][slot]), df[dc], dp[kb], 0, 0, 0);
       }
@@ -189,7 +188,7 @@ void attn_bwd_dq_kernel(AttnBwdProblem p) {
 #pragma unroll
         for (int db = 0; db < 2; ++db) {
           const int d = 32 * db + l32;
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(sm.kt[stage][d][u ^ vt_swz(d)]), as_bf16x8(w),
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(sm.kt[stage][d][u ^ col_swz(d)]), as_bf16x8(w),
                                                             acc[db], 0, 0, 0);
         }
       }
@@ -304,7 +303,7 @@ void attn_bwd_dkdv_kernel(AttnBwdProblem p) {
       const int row = 32 * qb + l32;
 #pragma unroll
       for (int dc = 0; dc < 4; ++dc) {
-        const int slot = (2 * dc + hi) ^ (row & 7);
+        const int slot = (2 * dc + hi) ^ row_swz(row);
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(sm.q[stage][row][slot]), kf[dc], s, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(sm.d[stage][row][slot]), vf[dc], dp, 0, 0, 0);
       }
@@ -322,7 +321,7 @@ void attn_bwd_dkdv_kernel(AttnBwdProblem p) {
 #pragma unroll
         for (int db = 0; db < 2; ++db) {
           const int d = 32 * db + l32;
-          const int slot = u ^ vt_swz(d);
+          const int slot = u ^ col_swz(d);
           dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(sm.dt[stage][d][slot]), as_bf16x8(pw), dva[db],
                                                             0, 0, 0);
           dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(sm.qt[stage][d][slot]), as_bf16x8(sw), dka[db],

@@ -27,6 +27,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
+// 16-byte slot swizzles of the 8 KiB tile images (64 rows of 8 x 16-byte units) that the
+// attention kernels copy linearly into LDS: unit u of row r sits at slot u ^ row_swz(r) in
+// row tiles (rows are keys or queries) and at slot u ^ col_swz(d) in transposed tiles (rows
+// are channels).  An MFMA operand read (ds_read_b128) has lane l read one unit of row
+// base + l % 32; the swizzle spreads each group of rows read together over distinct banks.
+#ifndef VGGT_TILE_SWZ
+#define VGGT_TILE_SWZ 2
+#endif
+__device__ __forceinline__ int row_swz(int r) { return VGGT_TILE_SWZ == 1 ? (r & 7) : ((r >> 1) & 7); }
+__device__ __forceinline__ int col_swz(int d) { return VGGT_TILE_SWZ == 1 ? ((d ^ (d >> 3)) & 7) : ((d >> 1) & 7); }
+
 // Workgroups are dealt round-robin to the 8 XCDs; this maps the hardware id w
 // of nwg workgroups to a logical id such that each XCD receives a contiguous
 // run of logical ids (consecutive work shares that XCD's L2).

@@ -43,11 +43,10 @@ __device__ __forceinline__ const T* key_ptr(const KeySrc& src, int64_t row, int6
 }
 
 __device__ __forceinline__ int rho_key(int i) { return (i & ~0xC) | ((i & 4) << 1) | ((i & 8) >> 1); }
-__device__ __forceinline__ int swz_vt(int d) { return (d ^ (d >> 3)) & 7; }
 
 // K (key j of sequence q at the row given by the KeySrc) -> KT [nseq][H][ntile][64 rows]
 // [8 slots of 16 bytes]: row r of tile
-// kt holds key 64*kt + rho(r), slot s holds its channels 8u..8u+7 with u = s ^ (r & 7).
+// kt holds key 64*kt + rho(r), slot s holds its channels 8u..8u+7 with u = s ^ row_swz(r).
 // Source key j lands on tile key key0 + j; tile keys below key0 keep what the buffer
 // holds (appending to a filled prefix), tile keys at or past key0 + len become zero.
 // With a table, pairs are rotated as in rope_apply_kernel (the position of a key on main
@@ -72,7 +71,7 @@ __global__ __launch_bounds__(NT) void k_tiles_kernel(KeySrc k, u32x4* __restrict
     const int r = i >> 3, slot = i & 7;
     const int key = tile * 64 + rho_key(r) - key0;  // source key
     if (key < 0) continue;
-    const int u = slot ^ (r & 7);
+    const int u = slot ^ row_swz(r);
     u32x4 w = {0u, 0u, 0u, 0u};
     if (key < len) {
       const int64_t row = key_row(k, sq, key);
@@ -131,7 +130,7 @@ __global__ __launch_bounds__(NT) void k_tiles_kernel(KeySrc k, u32x4* __restrict
 }
 
 // V (rows as for k_tiles_kernel) -> VT [nseq][H][ntile][64 channel rows][8 slots]: slot s of row d
-// holds tile keys 8u .. 8u+7 of channel d, u = s ^ swz_vt(d).  Source key j lands on tile
+// holds tile keys 8u .. 8u+7 of channel d, u = s ^ col_swz(d).  Source key j lands on tile
 // key key0 + j; tile keys below key0 keep their contents (a slot that straddles key0 is
 // merged with what the buffer holds), tile keys at or past key0 + len become zero.
 // grid (tiles written, H, nseq) as for k_tiles_kernel; the 64 x 64 tile is transposed
@@ -159,7 +158,7 @@ __global__ __launch_bounds__(NT) void v_tiles_kernel(KeySrc v, u32x4* __restrict
   for (int c = 0; c < 2; ++c) {
     const int i = threadIdx.x + c * NT;
     const int d = i >> 3, slot = i & 7;
-    const int u = slot ^ swz_vt(d);
+    const int u = slot ^ col_swz(d);
     const int kept = -kfirst - 8 * u;  // leading keys of this slot that stay as they are
     if (kept >= 8) continue;
     u32x4 w;
