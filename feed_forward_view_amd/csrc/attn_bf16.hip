@@ -104,6 +104,12 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // interleave hint for the scheduler: n x (1 MFMA, v VALU)
+#ifndef VGGT_IL_N
+#define VGGT_IL_N 8
+#endif
+#ifndef VGGT_IL_V
+#define VGGT_IL_V 8
+#endif
 #define VGGT_INTERLEAVE(n, v)                                  \
   _Pragma("unroll") for (int _i = 0; _i < (n); ++_i) {         \
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         \
@@ -398,14 +404,14 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
     if constexpr (QB == 2) {
       qk(s1, 1);
       float ls0 = soft(s0, false, 0.0f, p0);
-      VGGT_INTERLEAVE(8, 8);
+      VGGT_INTERLEAVE(VGGT_IL_N, VGGT_IL_V);
       if constexpr (masked) mask(s1, kbeg + t * BK);
       if (first || __any(!(ls0 <= kSumLimit))) ls0 = slow(s0, 0, first, p0);
       lsum[0] += ls0;
       read_v(stage);
       pv(p0, 0);
       float ls1 = soft(s1, false, 0.0f, p1);
-      VGGT_INTERLEAVE(8, 8);
+      VGGT_INTERLEAVE(VGGT_IL_N, VGGT_IL_V);
       if (first || __any(!(ls1 <= kSumLimit))) ls1 = slow(s1, QB - 1, first, p1);
       lsum[QB - 1] += ls1;
       pv(p1, QB - 1);
