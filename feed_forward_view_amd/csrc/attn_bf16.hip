@@ -23,12 +23,13 @@
 // the key index swapped) so that the S^T accumulator registers are, in order,
 // exactly the bf16 B operand of the P V product.
 //
-// Overlap.  On gfx950 a wave's own VALU instructions do not overlap its
-// MFMAs; VALU work of the other wave on the SIMD can: plain VALU (fma, add,
-// cvt) hides completely behind a running MFMA, exponentials mostly, dot2
-// not at all.  With two waves per SIMD that both mix the two kinds about a
-// third of the VALU time hides, so the loop keeps VALU work per tile to the
-// minimum (one exp per score, one cvt and one dot2 per score pair) and
+// Overlap.  On gfx950 a 32x32x16 MFMA issues every 32 clocks per SIMD and a
+// dependent accumulator chain costs nothing extra.  While it runs, plain VALU
+// work (fma, add, cvt) hides almost completely, from the same wave or the
+// other wave on the SIMD; v_exp_f32 (8 clocks per wave instruction) hides
+// about half behind the wave's own MFMAs and fully behind the other wave's;
+// v_dot2_f32_bf16 never overlaps an MFMA.  The loop therefore keeps VALU work
+// per tile to one exp per score and one cvt and one dot2 per score pair, and
 // interleaves each query block's exponentials with the other block's MFMAs.
 //
 // Softmax reference.  m starts at 0 and stays there while a row's scores stay
