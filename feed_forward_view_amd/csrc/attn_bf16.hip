@@ -360,15 +360,20 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
       delta = mx;
     }
     if (__any(delta != 0.0f)) {
-      const float alpha = __builtin_amdgcn_exp2f(-delta);
-      lsum[qb] *= alpha;
       mref[qb] += delta;
+      if (!first) {
+        // before the first tile O and l are still zero: only the reference
+        // moves (2^-delta overflows when the first tile moves it far down)
+        const float alpha = __builtin_amdgcn_exp2f(-delta);
+        lsum[qb] *= alpha;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        o[0][qb][r] *= alpha;
-        o[1][qb][r] *= alpha;
-        negm[qb][r] = -mref[qb];
+        for (int r = 0; r < 16; ++r) {
+          o[0][qb][r] *= alpha;
+          o[1][qb][r] *= alpha;
+        }
       }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) negm[qb][r] = -mref[qb];
     }
     return soft(s, true, delta, pf);
   };

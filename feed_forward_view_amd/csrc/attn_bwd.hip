@@ -172,6 +172,16 @@ void attn_bwd_dq_kernel(AttnBwdProblem p) {
         dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(sm.v[stage][row][slot]), df[dc], dp[kb], 0, 0, 0);
       }
     }
+    if (t == p.ntile - 1 && 64 * p.ntile > p.n) {
+      // keys past the end are zero rows, so their score would be the bare
+      // -lse2, whose exponential overflows when the row's log-normaliser lies
+      // far below zero (and then meets the zero K^T row as inf * 0)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (64 * t + 32 * kb + 16 * (r >> 3) + 8 * hi + (r & 7) >= p.n) s[kb][r] = -INFINITY;
+    }
     // dS^T as bf16 pairs: registers 8j..8j+7 of block kb are keys 32kb + 16j + 8hi + 0..7
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
