@@ -993,7 +993,7 @@ vggt_status ex_call(const ExArgs& a, vggt_dtype dt, int kv_splits, void* workspa
   g_last_error[0] = 0;
   if (!dtype_ok(dt)) return fail(VGGT_ERR_UNSUPPORTED, "unknown dtype %d", (int)dt);
   if (!tokens_ok(a.S, a.T, a.H) || a.Ta < 1 || a.Ta > a.T || a.E < 0 || a.E > kMaxExtra ||
-      (!a.global && a.E != 0))
+      (!a.global && a.E != 0) || (a.S == 0 && a.E != 0))
     return fail(VGGT_ERR_SHAPE, "bad shape S=%d T=%d T_active=%d n_extra=%d H=%d", a.S, a.T, a.Ta, a.E, a.H);
   if (kv_splits < 0 || kv_splits > kMaxSplits) return fail(VGGT_ERR_SHAPE, "kv_splits must be in [0, %d]", kMaxSplits);
   if (vggt_status s = check_norm(a.norm)) return s;

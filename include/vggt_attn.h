@@ -37,6 +37,12 @@
  *   - Device: the current HIP device must be gfx950 (VGGT_ERR_UNSUPPORTED).
  *   - Reentrancy: calls are reentrant; calls that share a workspace must be
  *     ordered on one stream by the caller.
+ *   - Empty calls: S = 0 (n = 0 for vggt_descriptor_cache_append, nq = 0 for
+ *     vggt_descriptor_cache_attn) is valid once the dtype and the other sizes
+ *     pass their checks: the call returns VGGT_OK without reading any pointer
+ *     or touching the device, and the workspace queries return 0.  The one
+ *     exception is vggt_global_attn_ex with n_extra > 0 and S = 0, which is
+ *     VGGT_ERR_SHAPE.
  */
 #ifndef VGGT_ATTN_H
 #define VGGT_ATTN_H
@@ -175,7 +181,8 @@ vggt_status vggt_global_attn_qknorm(const void* q, const void* k, const void* v,
  * rotation); the LayerNorm, if given, applies to them too.  kv_splits applies
  * to the frame tokens' queries; the extra tokens' queries (a separate launch
  * over the same prepared keys) always use the library's split choice.
- * n_extra in [0, 4096].  No output may overlap an input (VGGT_ERR_ALIAS).
+ * n_extra in [0, 4096], and 0 when S = 0.  No output may overlap an input
+ * (VGGT_ERR_ALIAS).
  *
  * Positions, scale, norm (NULL = none) and the workspace are as for
  * vggt_frame_attn_qknorm; `flags` of the workspace queries are

@@ -259,3 +259,51 @@ def test_backward_arguments(L):
     assert t(_p(A), _p(B), _p(C), _p(O), None, 0, 2, 8, 1, None, 100.0, 0.0, 0, _p(0x10000000), big, None) == NULL
     assert t(_p(A), _p(B), _p(C), _p(O), _p(A + 64), 0, 2, 8, 1, None, 100.0, 0.0, 0, _p(0x10000000), big,
              None) == ALIAS
+
+
+def test_empty_calls_are_noops(L):
+    """S = 0 (n = 0 / nq = 0 for the cache calls) returns OK without reading a
+    pointer or touching the device; workspace queries return 0.  Global
+    attention with extra tokens but no frames is rejected."""
+    BF16, F32 = 0, 1
+    norm = ffv.QkNorm(0x900000, 0x900100, 0x900200, 0x900300, 1e-5)
+    pn = ctypes.byref(norm)
+    for dt in (BF16, F32):
+        assert L.vggt_attn_rope(None, dt, 0, 8, 1, None, 100.0, None) == OK
+        assert L.vggt_frame_attn(None, None, None, None, dt, 0, 8, 1, None, 100.0, 0.0, None, 0, None) == OK
+        assert L.vggt_global_attn(None, None, None, None, dt, 0, 8, 1, None, 100.0, 0.0, 0, None, 0, None) == OK
+        assert L.vggt_frame_attn_qknorm(None, None, None, None, dt, 0, 8, 1, None, 100.0, 0.0, pn, None, 0, None) == OK
+        assert L.vggt_global_attn_qknorm(None, None, None, None, dt, 0, 8, 1, None, 100.0, 0.0, 0, pn, None, 0,
+                                         None) == OK
+        assert L.vggt_frame_attn_ex(None, None, None, None, dt, 0, 8, 6, 1, None, 100.0, 0.0, None, None, 0,
+                                    None) == OK
+        assert L.vggt_global_attn_ex(None, None, None, None, dt, 0, 8, 6, 1, None, None, None, None, 0, None, 100.0,
+                                     0.0, 0, None, None, 0, None) == OK
+        assert L.vggt_frame_attn_train(None, None, None, None, None, dt, 0, 8, 1, None, 100.0, 0.0, None, 0,
+                                       None) == OK
+        assert L.vggt_global_attn_train(None, None, None, None, None, dt, 0, 8, 1, None, 100.0, 0.0, 0, None, 0,
+                                        None) == OK
+        for back in (L.vggt_frame_attn_backward, L.vggt_global_attn_backward):
+            assert back(None, None, None, None, None, None, None, None, None, dt, 0, 8, 1, None, 100.0, 0.0, None,
+                        0, None) == OK
+        assert L.vggt_descriptor_pool(None, None, None, None, dt, 0, 14, 1, 3, 4, 2, 2, 2, None) == OK
+        assert L.vggt_descriptor_xattn(None, None, None, None, dt, 0, 8, 3, 1, 0.0, 0, None, 0, None) == OK
+        assert L.vggt_descriptor_cache_append(None, dt, 64, 1, 0, None, None, 0, None) == OK
+        assert L.vggt_descriptor_cache_attn(None, None, None, dt, 64, 1, 1, 0, 0.0, 0, None, 0, None) == OK
+        assert L.vggt_descriptor_chunked_xattn(None, None, None, dt, 64, 1, 0, 8, 3, 1, 0.0, None) == OK
+        # workspace queries
+        assert L.vggt_frame_attn_workspace(0, 8, 1, 1, dt) == 0
+        assert L.vggt_global_attn_workspace(0, 8, 1, 0, 1, dt) == 0
+        assert L.vggt_frame_attn_ex_workspace(0, 8, 6, 1, 1, dt) == 0
+        assert L.vggt_global_attn_ex_workspace(0, 8, 6, 0, 1, 0, 1, dt) == 0
+        assert L.vggt_descriptor_xattn_workspace(0, 8, 3, 1, 0, dt) == 0
+        assert L.vggt_descriptor_cache_attn_workspace(0, 1, 1, 0, dt) == 0
+        assert L.vggt_attn_backward_workspace(0, 8, 1, 1, 1, dt) == 0
+        # the size checks still run first
+        assert L.vggt_frame_attn(None, None, None, None, dt, 0, 0, 1, None, 100.0, 0.0, None, 0, None) == SHAPE
+        assert L.vggt_global_attn(None, None, None, None, dt, 0, 8, 0, None, 100.0, 0.0, 0, None, 0, None) == SHAPE
+        # extra tokens without frames
+        X = _p(0x800000)
+        assert L.vggt_global_attn_ex(None, None, None, None, dt, 0, 8, 6, 1, X, X, X, X, 2, None, 100.0, 0.0, 0,
+                                     None, None, 0, None) == SHAPE
+        assert L.vggt_global_attn_ex_workspace(0, 8, 6, 2, 1, 0, 1, dt) == 0

@@ -329,3 +329,16 @@ def test_split_count_independence_full_size():
     for o in outs[1:]:
         # different split counts only reorder fp32 sums: results agree to bf16 rounding
         assert (o - outs[0]).abs().max().item() <= 2.0 ** -7
+
+
+def test_empty_batch_through_the_binding():
+    # zero frames: empty CUDA tensors (null data pointers) in, empty results out
+    e = [torch.empty(0, 8, 2, 64, dtype=torch.bfloat16, device=dev()) for _ in range(4)]
+    q, k, v, g = e
+    assert ffv.vggt_frame_attn(q, k, v).shape == (0, 8, 2, 64)
+    assert ffv.vggt_global_attn(q, k, v).shape == (0, 8, 2, 64)
+    o, lse = ffv.vggt_global_attn_train(q, k, v)
+    assert o.shape == (0, 8, 2, 64) and lse.numel() == 0
+    dq, dk, dv = ffv.vggt_global_attn_backward(q, k, v, o, g, lse)
+    assert dq.shape == dk.shape == dv.shape == (0, 8, 2, 64)
+    torch.cuda.synchronize()
