@@ -202,6 +202,8 @@ def main() -> int:
         },
         "ms_per_layer": round(med["frame"] + med["global"], 4),
         "calls_ms_median": {c: round(x, 4) for c, x in med.items()},
+        "calls_ms_p10_p90": {c: [round(float(np.percentile(x, 10)), 4), round(float(np.percentile(x, 90)), 4)]
+                             for c, x in per_call.items()},
         "global_attention_tflops": round(g_tflops, 2),
         "global_frac_of_bf16_peak": round(g_tflops / PEAK_BF16_TFLOPS, 4),
         "frame_attention_tflops": round(flops["frame"] / (med["frame"] * 1e-3) / 1e12, 2),
@@ -219,7 +221,7 @@ def main() -> int:
             "traffic": profiled_traffic(),
         },
         "device": {"name": props.name, "cus": props.multi_processor_count,
-                   "arch": getattr(props, "gcnArchName", "")},
+                   "arch": getattr(props, "gcnArchName", ""), "max_clock_mhz": _max_clock_mhz()},
         "input_gen_s": round(gen_s, 2),
     }
 
@@ -236,11 +238,27 @@ def main() -> int:
     if not args.no_cpu_baseline:
         result["cpu_baseline"], result["parity_sample"] = cpu_baseline(wl, q, k, v, pos, Dn, ph, pw, go, fo, xo,
                                                                        args.cpu_row_stride)
+        # throughput ratio of the step on the GPU to the oracle on the host's cores
+        result["gpu_over_cpu_oracle"] = round(value / result["cpu_baseline"]["value"], 1)
     print(json.dumps(result), flush=True)
     return 0
 
 
 _FLUSH = None
+
+
+def _max_clock_mhz():
+    """Peak shader clock of device 0 from the HIP runtime (hipDeviceAttributeClockRate, kHz), or None."""
+    import ctypes
+
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        khz = ctypes.c_int(0)
+        if hip.hipDeviceGetAttribute(ctypes.byref(khz), 5, 0) != 0:  # 5 = hipDeviceAttributeClockRate
+            return None
+        return khz.value // 1000
+    except OSError:
+        return None
 
 
 def _flush_cache():
