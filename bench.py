@@ -38,8 +38,8 @@ PEAK_HBM_GBS = 8000.0
 # plain 1 GiB copy (profiles/attn_fwd_bf16_vggt-518-s32_counters.md).  Valid
 # only for the kernel source it was measured on.
 PROFILED_TRAFFIC = {
-    "kernel_source_sha256": "67953bfe1bd2c7c9e6c04b82598265da57cd0aaa18c00f9021a4fcd5cb04de58",
-    "read_bytes": 1331.7e6,
+    "kernel_source_sha256": "aeb10522fdeaaa7d44125fffccff9bd8625b4b73d848c4d447e5baf35a2b3c79",
+    "read_bytes": 1344.4e6,
     "write_bytes": 405.2e6,
 }
 
