@@ -11,24 +11,28 @@
 // position's rotation.
 //
 // Two kernels, no atomics:
-//   attn_bwd_dq_kernel    one wave per 32 queries, keys streamed in 64-key
-//                         tiles (K rows, V rows, K^T) through LDS:
+//   attn_bwd_dq_kernel    one wave per 32 queries (two 16-query blocks), keys
+//                         streamed in 64-key tiles (K rows, V rows, K^T)
+//                         through LDS:
 //                           S^T  = K Q^T - lse2      (accumulator input -lse2)
 //                           dP^T = V dO^T - D        (accumulator input -D)
 //                           dS^T = 2^(S^T) * dP^T
 //                           dQ^T += K^T dS^T
-//   attn_bwd_dkdv_kernel  one wave per 32 keys, queries streamed in 64-query
-//                         tiles (Q rows, dO rows, Q^T, dO^T, lse2, D):
+//   attn_bwd_dkdv_kernel  one wave per 32 keys (two 16-key blocks), queries
+//                         streamed in 64-query tiles (Q rows, dO rows, Q^T,
+//                         dO^T, lse2, D):
 //                           S  = Q K^T - lse2,  dP = dO V^T - D
 //                           dV^T += dO^T P,      dK^T += Q^T dS
-// Both use v_mfma_f32_32x32x16_bf16 with the layout tricks of the forward
-// kernel: row tiles hold their 64 rows in the order rho (bits 2 and 3
-// swapped), so the accumulator registers of a score block are, in order, the
-// bf16 operand of the next product; transposed tiles hold 8-row units per
-// 16-byte slot.  The query operand of the scores carries scale*log2(e) and is
+// Both use v_mfma_f32_16x16x32_bf16 with the layout of the forward kernel:
+// the accumulator registers of two 16-row score blocks are, in order, the
+// bf16 B operand of the next product for their 32-row chunk, because the
+// transposed tiles store each chunk's rows in that operand order.  (Under
+// sustained load this shape keeps a higher clock than 32x32x16 at the same
+// work.)  The query operand of the scores carries scale*log2(e) and is
 // rounded exactly as in the forward kernel, so the recomputed probabilities
 // match the saved log-normaliser.  Rows past the end are zero in every tile
-// and their -lse2 is -inf, so they contribute nothing.
+// and their -lse2 is -inf, so they contribute nothing; keys past the end are
+// masked in the dQ kernel's last tile.
 #include "common.h"
 
 namespace vggt {
@@ -51,14 +55,11 @@ __device__ __forceinline__ void wait_vmcnt() {
   else if constexpr (N == 9) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
 }
 
-__device__ __forceinline__ f32x16 splat(float x) {
-  f32x16 r;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) r[i] = x;
-  return r;
-}
-
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 w) { return __builtin_bit_cast(bf16x8, w); }
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
 
 // Rotate a dim pair back (transpose of the RoPE rotation), scale, store 4 dims of one row.
 __device__ __forceinline__ void store4(uint16_t* dst, const float* x, const f32x2* trow, int d0, float scale) {
@@ -89,7 +90,7 @@ struct SmemDq {
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dq_kernel(AttnBwdProblem p) {
   __shared__ SmemDq sm;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, g = lane >> 4;
   const int ntq = (p.n + BWG - 1) / BWG;
   const int nwg = ntq * p.H * p.nseq;
   int logical;
@@ -117,38 +118,50 @@ void attn_bwd_dq_kernel(AttnBwdProblem p) {
   };
   issue(0, 0);
 
-  // this lane's query, its rotated and scaled Q fragments and its dO fragments
-  const int qi = qt * BWG + wave * BW + l32;
-  const bool ok = qi < p.n;
-  const int64_t tok = tok0 + (ok ? qi : 0);
-  const f32x2* trow = p.rope_tab ? p.rope_tab + (int)(tok % p.rope_T) * 32 : nullptr;
-  bf16x8 qf[4], df[4];
+  // the wave's 32 queries as two 16-query blocks: this lane holds query 16qb + l16 of the
+  // wave, channels 32dc + 8g .. +7 of its rotated and scaled Q and of its dO
+  const int qw = qt * BWG + wave * BW;
+  bf16x8 qf[2][2], df[2][2];
+  f32x4 nl[2], nd[2];
+  const f32x2* trow[2];
 #pragma unroll
-  for (int dc = 0; dc < 4; ++dc) {
-    const int d0 = 16 * dc + 8 * hi;
-    u32x4 w = *(const u32x4*)((const uint16_t*)p.q + tok * p.tok_stride + head * D + d0);
-    u32x4 g = *(const u32x4*)((const uint16_t*)p.dout + tok * p.tok_stride + head * D + d0);
-    if (!ok) w = g = u32x4{0u, 0u, 0u, 0u};
-    u32x4 r;
+  for (int qb = 0; qb < 2; ++qb) {
+    const int qi = qw + 16 * qb + l16;
+    const bool ok = qi < p.n;
+    const int64_t tok = tok0 + (ok ? qi : 0);
+    trow[qb] = p.rope_tab ? p.rope_tab + (int)(tok % p.rope_T) * 32 : nullptr;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      float x = lo_bf16(w[e]), y = hi_bf16(w[e]);
-      if (trow) {
-        const f32x2 cs = trow[(d0 >> 1) + e];
-        const float x2 = __builtin_fmaf(x, cs[0], -y * cs[1]);
-        const float y2 = __builtin_fmaf(x, cs[1], y * cs[0]);
-        x = x2;
-        y = y2;
+    for (int dc = 0; dc < 2; ++dc) {
+      const int d0 = 32 * dc + 8 * g;
+      u32x4 w = *(const u32x4*)((const uint16_t*)p.q + tok * p.tok_stride + head * D + d0);
+      u32x4 gr = *(const u32x4*)((const uint16_t*)p.dout + tok * p.tok_stride + head * D + d0);
+      if (!ok) w = gr = u32x4{0u, 0u, 0u, 0u};
+      u32x4 r;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float x = lo_bf16(w[e]), y = hi_bf16(w[e]);
+        if (trow[qb]) {
+          const f32x2 cs = trow[qb][(d0 >> 1) + e];
+          const float x2 = __builtin_fmaf(x, cs[0], -y * cs[1]);
+          const float y2 = __builtin_fmaf(x, cs[1], y * cs[0]);
+          x = x2;
+          y = y2;
+        }
+        r[e] = pack_bf16x2(x * p.scale_log2, y * p.scale_log2);
       }
-      r[e] = pack_bf16x2(x * p.scale_log2, y * p.scale_log2);
+      qf[qb][dc] = as_bf16x8(r);
+      df[qb][dc] = as_bf16x8(gr);
     }
-    qf[dc] = as_bf16x8(r);
-    df[dc] = as_bf16x8(g);
+    const float l2 = ok ? p.lse2[sbase + qi] : -INFINITY, ds = ok ? p.dsum[sbase + qi] : 0.0f;
+    nl[qb] = f32x4{l2, l2, l2, l2};
+    nd[qb] = f32x4{ds, ds, ds, ds};
   }
-  const f32x16 nl = splat(ok ? p.lse2[sbase + qi] : -INFINITY);
-  const f32x16 nd = splat(ok ? p.dsum[sbase + qi] : 0.0f);
 
-  f32x16 acc[2] = {splat(0.0f), splat(0.0f)};  // dQ^T [db]: dims 32db + ..., this lane's query
+  f32x4 acc[2][4];  // dQ^T [qb][db]: channels 16db + 4g + r of the lane's query
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int db = 0; db < 4; ++db) acc[qb][db] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   for (int t = 0; t < p.ntile; ++t) {
     const int stage = t & 1;
     if (t + 1 < p.ntile) {
@@ -159,59 +172,72 @@ void attn_bwd_dq_kernel(AttnBwdProblem p) {
       wait_vmcnt<0>();
     }
     __syncthreads();
-    f32x16 s[2], dp[2];
+    bf16x8 kf[4][2], vf[4][2], ktf[2][4];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int row = 32 * kb + l32;
-      s[kb] = nl;
-      dp[kb] = nd;
+    for (int kb = 0; kb < 4; ++kb) {
+      const int row = 16 * kb + l16;
 #pragma unroll
-      for (int dc = 0; dc < 4; ++dc) {
-        const int slot = (2 * dc + hi) ^ row_swz(row);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(sm.k[stage][row][slot]), qf[dc], s[kb], 0, 0, 0);
-        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(sm.v[stage][row][slot]), df[dc], dp[kb], 0, 0, 0);
+      for (int dc = 0; dc < 2; ++dc) {
+        const int slot = (4 * dc + g) ^ row_swz(row);
+        kf[kb][dc] = as_bf16x8(sm.k[stage][row][slot]);
+        vf[kb][dc] = as_bf16x8(sm.v[stage][row][slot]);
       }
     }
-    if (t == p.ntile - 1 && 64 * p.ntile > p.n) {
-      // keys past the end are zero rows, so their score would be the bare
-      // -lse2, whose exponential overflows when the row's log-normaliser lies
-      // far below zero (and then meets the zero K^T row as inf * 0)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (64 * t + 32 * kb + 16 * (r >> 3) + 8 * hi + (r & 7) >= p.n) s[kb][r] = -INFINITY;
-    }
-    // dS^T as bf16 pairs: registers 8j..8j+7 of block kb are keys 32kb + 16j + 8hi + 0..7
+      for (int db = 0; db < 4; ++db) {
+        const int d = 16 * db + l16;
+        ktf[c][db] = as_bf16x8(sm.kt[stage][d][(4 * c + g) ^ col_swz(d)]);
+      }
+    const bool tail = t == p.ntile - 1 && 64 * p.ntile > p.n;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int qb = 0; qb < 2; ++qb) {
+      // S^T and dP^T of this query block: lane holds keys 16kb + 4g + r of its query
+      f32x4 s[4], dp[4];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int kb = 0; kb < 4; ++kb) {
+        s[kb] = mfma16(kf[kb][0], qf[qb][0], nl[qb]);
+        s[kb] = mfma16(kf[kb][1], qf[qb][1], s[kb]);
+        dp[kb] = mfma16(vf[kb][0], df[qb][0], nd[qb]);
+        dp[kb] = mfma16(vf[kb][1], df[qb][1], dp[kb]);
+      }
+      if (tail) {
+        // keys past the end are zero rows, so their score would be the bare
+        // -lse2, whose exponential overflows when the row's log-normaliser lies
+        // far below zero (and then meets the zero K^T row as inf * 0)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (64 * t + 16 * kb + 4 * g + r >= p.n) s[kb][r] = -INFINITY;
+      }
+      // dS^T = P dP^T as the bf16 B operand of dQ^T += K^T dS^T, chunk by chunk of 32 keys
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
         u32x4 w;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int r = 8 * j + 2 * e;
+          const int kb = 2 * c + (e >> 1), r = 2 * (e & 1);
           w[e] = pack_bf16x2(__builtin_amdgcn_exp2f(s[kb][r]) * dp[kb][r],
                              __builtin_amdgcn_exp2f(s[kb][r + 1]) * dp[kb][r + 1]);
         }
-        const int u = 4 * kb + 2 * j + hi;
 #pragma unroll
-        for (int db = 0; db < 2; ++db) {
-          const int d = 32 * db + l32;
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(sm.kt[stage][d][u ^ col_swz(d)]), as_bf16x8(w),
-                                                            acc[db], 0, 0, 0);
-        }
+        for (int db = 0; db < 4; ++db) acc[qb][db] = mfma16(ktf[c][db], as_bf16x8(w), acc[qb][db]);
       }
-  }
-  if (!ok) return;
-  uint16_t* dst = (uint16_t*)p.dq + tok * p.tok_stride + head * D;
-#pragma unroll
-  for (int db = 0; db < 2; ++db)
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const float x[4] = {acc[db][4 * a], acc[db][4 * a + 1], acc[db][4 * a + 2], acc[db][4 * a + 3]};
-      store4(dst, x, trow, 32 * db + 8 * a + 4 * hi, p.scale);
     }
+  }
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int qi = qw + 16 * qb + l16;
+    if (qi >= p.n) continue;
+    uint16_t* dst = (uint16_t*)p.dq + (tok0 + qi) * p.tok_stride + head * D;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const float x[4] = {acc[qb][db][0], acc[qb][db][1], acc[qb][db][2], acc[qb][db][3]};
+      store4(dst, x, trow[qb], 16 * db + 4 * g, p.scale);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -229,7 +255,7 @@ struct SmemDkv {
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dkdv_kernel(AttnBwdProblem p) {
   __shared__ SmemDkv sm;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, g = lane >> 4;
   const int ntk = (p.n + BWG - 1) / BWG;
   const int nwg = ntk * p.H * p.nseq;
   int logical;
@@ -266,23 +292,32 @@ void attn_bwd_dkdv_kernel(AttnBwdProblem p) {
   };
   issue(0, 0);
 
-  // this lane's key: rotated K and V fragments (B operands of S = Q K^T and dP = dO V^T)
-  const int kj = kt * BWG + wave * BW + l32;
-  const bool ok = kj < p.n;
-  const int64_t tok = tok0 + (ok ? kj : 0);
-  bf16x8 kf[4], vf[4];
+  // the wave's 32 keys as two 16-key blocks: this lane holds key 16kb + l16 of the wave,
+  // channels 32dc + 8g .. +7 of its rotated K and of its V (B operands of S = Q K^T and
+  // dP = dO V^T)
+  const int kw = kt * BWG + wave * BW;
+  bf16x8 kf[2][2], vf[2][2];
 #pragma unroll
-  for (int dc = 0; dc < 4; ++dc) {
-    const int d0 = 16 * dc + 8 * hi;
-    u32x4 a = *(const u32x4*)((const uint16_t*)p.kr + tok * p.tok_stride + head * D + d0);
-    u32x4 b = *(const u32x4*)((const uint16_t*)p.v + tok * p.tok_stride + head * D + d0);
-    if (!ok) a = b = u32x4{0u, 0u, 0u, 0u};
-    kf[dc] = as_bf16x8(a);
-    vf[dc] = as_bf16x8(b);
+  for (int kb = 0; kb < 2; ++kb) {
+    const int kj = kw + 16 * kb + l16;
+    const bool ok = kj < p.n;
+    const int64_t tok = tok0 + (ok ? kj : 0);
+#pragma unroll
+    for (int dc = 0; dc < 2; ++dc) {
+      const int d0 = 32 * dc + 8 * g;
+      u32x4 a = *(const u32x4*)((const uint16_t*)p.kr + tok * p.tok_stride + head * D + d0);
+      u32x4 b = *(const u32x4*)((const uint16_t*)p.v + tok * p.tok_stride + head * D + d0);
+      if (!ok) a = b = u32x4{0u, 0u, 0u, 0u};
+      kf[kb][dc] = as_bf16x8(a);
+      vf[kb][dc] = as_bf16x8(b);
+    }
   }
 
-  f32x16 dka[2] = {splat(0.0f), splat(0.0f)};  // dK^T [db], this lane's key
-  f32x16 dva[2] = {splat(0.0f), splat(0.0f)};  // dV^T [db]
+  f32x4 dka[2][4], dva[2][4];  // dK^T, dV^T [kb][db]: channels 16db + 4g + r of the lane's key
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int db = 0; db < 4; ++db) dka[kb][db] = dva[kb][db] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   for (int t = 0; t < p.ntile; ++t) {
     const int stage = t & 1;
     if (t + 1 < p.ntile) {
@@ -293,67 +328,76 @@ void attn_bwd_dkdv_kernel(AttnBwdProblem p) {
       wait_vmcnt<0>();
     }
     __syncthreads();
+    // the tile's 64 queries as two 32-query chunks c, each two 16-query blocks
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      // accumulator inputs: -lse2 and -D of the queries of registers r: 32qb + 16(r/8) + 8hi + r%8
-      f32x16 s, dp;
+    for (int c = 0; c < 2; ++c) {
+      f32x4 s[2][2], dp[2][2];  // [block 2c + i][kb]: queries 16(2c+i) + 4g + r, the lane's key
 #pragma unroll
-      for (int h8 = 0; h8 < 2; ++h8) {
-        const int q0 = 32 * qb + 16 * h8 + 8 * hi;
-        const f32x4 l0 = *(const f32x4*)&sm.st[stage][0][q0], l1 = *(const f32x4*)&sm.st[stage][0][q0 + 4];
-        const f32x4 d0 = *(const f32x4*)&sm.st[stage][1][q0], d1 = *(const f32x4*)&sm.st[stage][1][q0 + 4];
+      for (int i = 0; i < 2; ++i) {
+        const int qb = 2 * c + i, row = 16 * qb + l16;
+        // accumulator inputs: -lse2 and -D of the register's queries 16qb + 4g + r
+        const f32x4 nl = *(const f32x4*)&sm.st[stage][0][16 * qb + 4 * g];
+        const f32x4 nd = *(const f32x4*)&sm.st[stage][1][16 * qb + 4 * g];
+        bf16x8 qr[2], dr[2];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          s[8 * h8 + e] = l0[e];
-          s[8 * h8 + 4 + e] = l1[e];
-          dp[8 * h8 + e] = d0[e];
-          dp[8 * h8 + 4 + e] = d1[e];
+        for (int dc = 0; dc < 2; ++dc) {
+          const int slot = (4 * dc + g) ^ row_swz(row);
+          qr[dc] = as_bf16x8(sm.q[stage][row][slot]);
+          dr[dc] = as_bf16x8(sm.d[stage][row][slot]);
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          s[i][kb] = mfma16(qr[0], kf[kb][0], nl);
+          s[i][kb] = mfma16(qr[1], kf[kb][1], s[i][kb]);
+          dp[i][kb] = mfma16(dr[0], vf[kb][0], nd);
+          dp[i][kb] = mfma16(dr[1], vf[kb][1], dp[i][kb]);
         }
       }
-      const int row = 32 * qb + l32;
+      // P and dS = P dP as the bf16 B operands (queries of chunk c in operand order) of
+      // dV^T += dO^T P and dK^T += Q^T dS
+      bf16x8 dtf[4], qtf[4];
 #pragma unroll
-      for (int dc = 0; dc < 4; ++dc) {
-        const int slot = (2 * dc + hi) ^ row_swz(row);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(sm.q[stage][row][slot]), kf[dc], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(sm.d[stage][row][slot]), vf[dc], dp, 0, 0, 0);
+      for (int db = 0; db < 4; ++db) {
+        const int d = 16 * db + l16;
+        const int slot = (4 * c + g) ^ col_swz(d);
+        dtf[db] = as_bf16x8(sm.dt[stage][d][slot]);
+        qtf[db] = as_bf16x8(sm.qt[stage][d][slot]);
       }
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
+      for (int kb = 0; kb < 2; ++kb) {
         u32x4 pw, sw;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int r = 8 * c + 2 * e;
-          const float p0 = __builtin_amdgcn_exp2f(s[r]), p1 = __builtin_amdgcn_exp2f(s[r + 1]);
+          const int i = e >> 1, r = 2 * (e & 1);
+          const float p0 = __builtin_amdgcn_exp2f(s[i][kb][r]), p1 = __builtin_amdgcn_exp2f(s[i][kb][r + 1]);
           pw[e] = pack_bf16x2(p0, p1);
-          sw[e] = pack_bf16x2(p0 * dp[r], p1 * dp[r + 1]);
+          sw[e] = pack_bf16x2(p0 * dp[i][kb][r], p1 * dp[i][kb][r + 1]);
         }
-        const int u = 4 * qb + 2 * c + hi;
 #pragma unroll
-        for (int db = 0; db < 2; ++db) {
-          const int d = 32 * db + l32;
-          const int slot = u ^ col_swz(d);
-          dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(sm.dt[stage][d][slot]), as_bf16x8(pw), dva[db],
-                                                            0, 0, 0);
-          dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(sm.qt[stage][d][slot]), as_bf16x8(sw), dka[db],
-                                                            0, 0, 0);
+        for (int db = 0; db < 4; ++db) {
+          dva[kb][db] = mfma16(dtf[db], as_bf16x8(pw), dva[kb][db]);
+          dka[kb][db] = mfma16(qtf[db], as_bf16x8(sw), dka[kb][db]);
         }
       }
     }
   }
-  if (!ok) return;
-  const f32x2* trow = p.rope_tab ? p.rope_tab + (int)(tok % p.rope_T) * 32 : nullptr;
-  uint16_t* dkp = (uint16_t*)p.dk + tok * p.tok_stride + head * D;
-  uint16_t* dvp = (uint16_t*)p.dv + tok * p.tok_stride + head * D;
 #pragma unroll
-  for (int db = 0; db < 2; ++db)
+  for (int kb = 0; kb < 2; ++kb) {
+    const int kj = kw + 16 * kb + l16;
+    if (kj >= p.n) continue;
+    const int64_t tok = tok0 + kj;
+    const f32x2* trow = p.rope_tab ? p.rope_tab + (int)(tok % p.rope_T) * 32 : nullptr;
+    uint16_t* dkp = (uint16_t*)p.dk + tok * p.tok_stride + head * D;
+    uint16_t* dvp = (uint16_t*)p.dv + tok * p.tok_stride + head * D;
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const int d0 = 32 * db + 8 * a + 4 * hi;
-      const float xk[4] = {dka[db][4 * a], dka[db][4 * a + 1], dka[db][4 * a + 2], dka[db][4 * a + 3]};
-      const float xv[4] = {dva[db][4 * a], dva[db][4 * a + 1], dva[db][4 * a + 2], dva[db][4 * a + 3]};
+    for (int db = 0; db < 4; ++db) {
+      const int d0 = 16 * db + 4 * g;
+      const float xk[4] = {dka[kb][db][0], dka[kb][db][1], dka[kb][db][2], dka[kb][db][3]};
+      const float xv[4] = {dva[kb][db][0], dva[kb][db][1], dva[kb][db][2], dva[kb][db][3]};
       store4(dkp, xk, trow, d0, p.scale);
       store4(dvp, xv, nullptr, d0, 1.0f);
     }
+  }
 }
 
 // ---------------------------------------------------------------------------

@@ -321,12 +321,12 @@ hipError_t run_call(const Layout& L, vggt::AttnProblem p, vggt_dtype dt, int nse
       p.rope_tab = (const vggt::f32x2*)table;
       p.rope_T = rope_T;
     }
-    e = vggt::launch_k_tiles_bf16(vggt::kTiles16, vggt::contiguous_keys(p.k, (int)nk), ws + L.kt, nseq, (int)nk, H,
+    e = vggt::launch_k_tiles_bf16(vggt::contiguous_keys(p.k, (int)nk), ws + L.kt, nseq, (int)nk, H,
                                   table, rope_T,
                                   norm ? norm->k_gamma : nullptr, norm ? norm->k_beta : nullptr,
                                   norm ? norm->eps : 0.0f, st);
     if (e == hipSuccess)
-      e = vggt::launch_v_tiles_bf16(vggt::kTiles16, vggt::contiguous_keys(p.v, (int)nk), ws + L.vt, nseq, (int)nk, H,
+      e = vggt::launch_v_tiles_bf16(vggt::contiguous_keys(p.v, (int)nk), ws + L.vt, nseq, (int)nk, H,
                                     st);
     if (e != hipSuccess) return e;
     p.k = ws + L.kt;
@@ -911,10 +911,10 @@ hipError_t run_ex(const ExLayout& L, const ExArgs& a, vggt_dtype dt, char* ws, h
       p.q_ln_b = a.norm->q_beta;
       p.ln_eps = a.norm->eps;
     }
-    e = vggt::launch_k_tiles_bf16(vggt::kTiles16, ks, ws + L.kt, L.nseq_k, (int)L.nk, H, table, a.T,
+    e = vggt::launch_k_tiles_bf16(ks, ws + L.kt, L.nseq_k, (int)L.nk, H, table, a.T,
                                   a.norm ? a.norm->k_gamma : nullptr, a.norm ? a.norm->k_beta : nullptr,
                                   a.norm ? a.norm->eps : 0.0f, st);
-    if (e == hipSuccess) e = vggt::launch_v_tiles_bf16(vggt::kTiles16, vs, ws + L.vt, L.nseq_k, (int)L.nk, H, st);
+    if (e == hipSuccess) e = vggt::launch_v_tiles_bf16(vs, ws + L.vt, L.nseq_k, (int)L.nk, H, st);
     if (e != hipSuccess) return e;
     p.k = ws + L.kt;
     p.vt = ws + L.vt;
@@ -1199,23 +1199,23 @@ vggt_status attn_backward(bool global, const void* q, const void* k, const void*
     char* tqt = ws + L.tiles[5];
     char* tdot = ws + L.tiles[6];
     const int n = L.n, ns = L.nseq;
-    e = vggt::launch_k_tiles_bf16(vggt::kTiles32, vggt::contiguous_keys(k, n), tk, ns, n, H, table, T, nullptr,
+    e = vggt::launch_k_tiles_bf16(vggt::contiguous_keys(k, n), tk, ns, n, H, table, T, nullptr,
                                   nullptr, 0.0f, st);
     if (e == hipSuccess)
-      e = vggt::launch_k_tiles_bf16(vggt::kTiles32, vggt::contiguous_keys(v, n), tv, ns, n, H, nullptr, 1, nullptr,
+      e = vggt::launch_k_tiles_bf16(vggt::contiguous_keys(v, n), tv, ns, n, H, nullptr, 1, nullptr,
                                     nullptr, 0.0f, st);
     if (e == hipSuccess)
-      e = vggt::launch_v_tiles_bf16(vggt::kTiles32, vggt::contiguous_keys(kr, n), tkt, ns, n, H, st);
+      e = vggt::launch_v_tiles_bf16(vggt::contiguous_keys(kr, n), tkt, ns, n, H, st);
     if (e == hipSuccess)
-      e = vggt::launch_k_tiles_bf16(vggt::kTiles32, vggt::contiguous_keys(q, n), tq, ns, n, H, table, T, nullptr, nullptr, 0.0f, st,
+      e = vggt::launch_k_tiles_bf16(vggt::contiguous_keys(q, n), tq, ns, n, H, table, T, nullptr, nullptr, 0.0f, st,
                                     c);
     if (e == hipSuccess)
-      e = vggt::launch_k_tiles_bf16(vggt::kTiles32, vggt::contiguous_keys(dout, n), tdo, ns, n, H, nullptr, 1, nullptr, nullptr, 0.0f,
+      e = vggt::launch_k_tiles_bf16(vggt::contiguous_keys(dout, n), tdo, ns, n, H, nullptr, 1, nullptr, nullptr, 0.0f,
                                     st);
     if (e == hipSuccess)
-      e = vggt::launch_v_tiles_bf16(vggt::kTiles32, vggt::contiguous_keys(qr, n), tqt, ns, n, H, st);
+      e = vggt::launch_v_tiles_bf16(vggt::contiguous_keys(qr, n), tqt, ns, n, H, st);
     if (e == hipSuccess)
-      e = vggt::launch_v_tiles_bf16(vggt::kTiles32, vggt::contiguous_keys(dout, n), tdot, ns, n, H, st);
+      e = vggt::launch_v_tiles_bf16(vggt::contiguous_keys(dout, n), tdot, ns, n, H, st);
     if (e != hipSuccess) return device_error("backward tile pre-pass", e);
     vggt::AttnBwdProblem p;
     std::memset(&p, 0, sizeof(p));

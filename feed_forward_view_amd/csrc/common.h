@@ -87,8 +87,8 @@ struct AttnProblem {
 // Attention gradients (bf16).  Sequences, strides and counts as in
 // AttnProblem with nq == nk and q/k sequences T tokens apart (frame) or one
 // sequence (global).  Tile buffers: [nseq][H][ntile][64 x 64] in the forward
-// kernel's layouts -- "row" tiles as its K tiles (rows in key order rho),
-// "transposed" tiles as its V^T tiles.
+// kernel's layouts -- "row" tiles as its K tiles, "transposed" tiles as its
+// V^T tiles.
 struct AttnBwdProblem {
   const void* q;           // [tokens][H][64] bf16: Q fragments of the dQ kernel
   const void* dout;        // [tokens][H][64] bf16: dO fragments of the dQ kernel
@@ -156,24 +156,19 @@ inline KeySrc contiguous_keys(const void* k, int len) {
   return s;
 }
 
-// Key orders of the 64-key operand tiles: kTiles16 for the forward kernel's
-// 16x16x32 MFMA operands, kTiles32 for the gradient kernels' 32x32x16 operands.
-enum TileLayout { kTiles16 = 0, kTiles32 = 1 };
-
 // K -> tiles for nseq sequences of len keys (RoPE position of a main row r is
 // r % rope_T; extra rows are not rotated), with an optional per-head LayerNorm.
-hipError_t launch_k_tiles_bf16(TileLayout layout, const KeySrc& k, void* kt, int nseq, int len, int H,
-                               const void* table, int rope_T, const float* ln_g, const float* ln_b, float ln_eps,
-                               hipStream_t stream, float out_scale = 1.0f);
+hipError_t launch_k_tiles_bf16(const KeySrc& k, void* kt, int nseq, int len, int H, const void* table, int rope_T,
+                               const float* ln_g, const float* ln_b, float ln_eps, hipStream_t stream,
+                               float out_scale = 1.0f);
 // Per-head LayerNorm of fp32 [n_tok][H][64] (src may equal dst).
 hipError_t launch_layer_norm_f32(const float* src, float* dst, int64_t n_tok, int H, const float* g, const float* b,
                                  float eps, hipStream_t stream);
-hipError_t launch_v_tiles_bf16(TileLayout layout, const KeySrc& v, void* vt, int nseq, int len, int H,
-                               hipStream_t stream);
+hipError_t launch_v_tiles_bf16(const KeySrc& v, void* vt, int nseq, int len, int H, hipStream_t stream);
 // fp32 rows of a key source gathered into a contiguous [nseq*len][H][64] copy.
 hipError_t launch_gather_keys_f32(const KeySrc& src, float* dst, int nseq, int len, int H, hipStream_t stream);
-// Append n keys (K and V [n][H][64] bf16) to single-sequence kTiles16 tile buffers that
-// own dst_ntile tiles per head, at key offset key0; keys of the last tile past key0 + n are
+// Append n keys (K and V [n][H][64] bf16) to single-sequence tile buffers that own
+// dst_ntile tiles per head, at key offset key0; keys of the last tile past key0 + n are
 // zeroed, keys below key0 are kept.
 hipError_t launch_tiles_append_bf16(const void* k, const void* v, void* kt, void* vt, int dst_ntile, int key0, int n,
                                     int H, hipStream_t stream);

@@ -13,11 +13,10 @@
 //  v_tiles_kernel     V -> 64-key tiles of V^T in an attention kernel's LDS
 //                     order.
 // Each tile is 8 KiB and the attention kernels copy it linearly into LDS.
-// Two orders (TileLayout): kTiles16 for the forward kernel's 16x16x32 MFMA
-// operands (row tiles in key order; V^T units holding the keys of a 32-key
-// chunk in that kernel's operand order) and kTiles32 for the gradient
-// kernels' 32x32x16 operands (row tiles in the key order rho; V^T units of 8
-// consecutive keys).
+// The order serves their 16x16x32 MFMA operands: row tiles hold their rows in
+// order; a transposed tile's unit of 8 rows holds rows 4g..4g+3 and
+// 16+4g..16+4g+3 of a 32-row chunk, the order in which a 16x16x32 score block
+// pair, read register by register, forms the next product's B operand.
 #include "common.h"
 
 namespace vggt {
@@ -47,21 +46,16 @@ __device__ __forceinline__ const T* key_ptr(const KeySrc& src, int64_t row, int6
   return row >= 0 ? (const T*)src.main + row * row_elems : (const T*)src.extra + (-1 - row) * row_elems;
 }
 
-__device__ __forceinline__ int rho_key(int i) { return (i & ~0xC) | ((i & 4) << 1) | ((i & 8) >> 1); }
-
-// Tile key of the first of the two keys that 32-bit word e (0..3) of V^T unit u (0..7) holds.
-// kTiles32: keys 8u .. 8u+7 in order.  kTiles16: unit u holds operand keys 8g .. 8g+7 of chunk
-// c = u / 4 (g = u % 4), which stand for chunk keys 4g .. 4g+3 and 16+4g .. 16+4g+3.
-template <TileLayout L>
+// Tile key of the first of the two keys that 32-bit word e (0..3) of V^T unit u (0..7) holds:
+// unit u holds operand keys 8g .. 8g+7 of chunk c = u / 4 (g = u % 4), which stand for chunk
+// keys 4g .. 4g+3 and 16+4g .. 16+4g+3.
 __device__ __forceinline__ int vt_word_key(int u, int e) {
-  if constexpr (L == kTiles32) return 8 * u + 2 * e;
-  else return 32 * (u >> 2) + 4 * (u & 3) + 2 * (e & 1) + 16 * (e >> 1);
+  return 32 * (u >> 2) + 4 * (u & 3) + 2 * (e & 1) + 16 * (e >> 1);
 }
 
 // K (key j of sequence q at the row given by the KeySrc) -> KT [nseq][H][ntile][64 rows]
 // [8 slots of 16 bytes]: row r of tile
-// kt holds key 64*kt + r (kTiles16) or 64*kt + rho(r) (kTiles32), slot s holds its channels
-// 8u..8u+7 with u = s ^ row_swz(r).
+// kt holds key 64*kt + r, slot s holds its channels 8u..8u+7 with u = s ^ row_swz(r).
 // Source key j lands on tile key key0 + j; tile keys below key0 keep what the buffer
 // holds (appending to a filled prefix), tile keys at or past key0 + len become zero.
 // With a table, pairs are rotated as in rope_apply_kernel (the position of a key on main
@@ -72,7 +66,6 @@ __device__ __forceinline__ int vt_word_key(int u, int e) {
 // LayerNorm (gamma ln_g, beta ln_b, eps ln_eps; the 8 lanes that hold one key row
 // reduce its 64 channels by xor shuffles), then rotated, then multiplied by out_scale
 // and rounded once to bf16.
-template <TileLayout L>
 __global__ __launch_bounds__(NT) void k_tiles_kernel(KeySrc k, u32x4* __restrict__ kt_out,
                                                      int len, int H, const f32x2* __restrict__ table, int rope_T,
                                                      int key0, int dst_ntile, const float* __restrict__ ln_g,
@@ -85,7 +78,7 @@ __global__ __launch_bounds__(NT) void k_tiles_kernel(KeySrc k, u32x4* __restrict
   for (int c = 0; c < 2; ++c) {
     const int i = threadIdx.x + c * NT;
     const int r = i >> 3, slot = i & 7;
-    const int key = tile * 64 + (L == kTiles16 ? r : rho_key(r)) - key0;  // source key
+    const int key = tile * 64 + r - key0;  // source key
     if (key < 0) continue;
     const int u = slot ^ row_swz(r);
     u32x4 w = {0u, 0u, 0u, 0u};
@@ -152,7 +145,6 @@ __global__ __launch_bounds__(NT) void k_tiles_kernel(KeySrc k, u32x4* __restrict
 // become zero.
 // grid (tiles written, H, nseq) as for k_tiles_kernel; the 64 x 64 tile is transposed
 // through LDS.
-template <TileLayout L>
 __global__ __launch_bounds__(NT) void v_tiles_kernel(KeySrc v, u32x4* __restrict__ vt_out,
                                                      int len, int H, int key0, int dst_ntile) {
   __shared__ uint32_t tile_s[64][33];  // [key][channel pair], padded
@@ -182,7 +174,7 @@ __global__ __launch_bounds__(NT) void v_tiles_kernel(KeySrc v, u32x4* __restrict
     bool all_kept = true, any_kept = false;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int j0 = vt_word_key<L>(u, e);  // keys j0, j0+1 of channel d
+      const int j0 = vt_word_key(u, e);  // keys j0, j0+1 of channel d
       const uint32_t a = tile_s[j0][d >> 1], b = tile_s[j0 + 1][d >> 1];
       w[e] = (d & 1) ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
       keep[e] = (j0 + 1 < kept) ? 0xFFFFFFFFu : (j0 < kept ? 0x0000FFFFu : 0u);
@@ -221,30 +213,21 @@ hipError_t launch_rope_table(const int32_t* pos_yx, int T, double base, void* ta
   return hipGetLastError();
 }
 
-hipError_t launch_k_tiles_bf16(TileLayout layout, const KeySrc& k, void* kt, int nseq, int len, int H,
-                               const void* table, int rope_T, const float* ln_g, const float* ln_b, float ln_eps,
-                               hipStream_t stream, float out_scale) {
+hipError_t launch_k_tiles_bf16(const KeySrc& k, void* kt, int nseq, int len, int H, const void* table, int rope_T,
+                               const float* ln_g, const float* ln_b, float ln_eps, hipStream_t stream,
+                               float out_scale) {
   if (nseq <= 0 || len <= 0) return hipSuccess;
   const int ntile = (len + 63) / 64;
-  const dim3 grid((unsigned)ntile, (unsigned)H, (unsigned)nseq);
-  if (layout == kTiles16)
-    hipLaunchKernelGGL(k_tiles_kernel<kTiles16>, grid, dim3(NT), 0, stream, k, (u32x4*)kt, len, H,
-                       (const f32x2*)table, rope_T, 0, ntile, ln_g, ln_b, ln_eps, out_scale);
-  else
-    hipLaunchKernelGGL(k_tiles_kernel<kTiles32>, grid, dim3(NT), 0, stream, k, (u32x4*)kt, len, H,
-                       (const f32x2*)table, rope_T, 0, ntile, ln_g, ln_b, ln_eps, out_scale);
+  hipLaunchKernelGGL(k_tiles_kernel, dim3((unsigned)ntile, (unsigned)H, (unsigned)nseq), dim3(NT), 0, stream, k,
+                     (u32x4*)kt, len, H, (const f32x2*)table, rope_T, 0, ntile, ln_g, ln_b, ln_eps, out_scale);
   return hipGetLastError();
 }
 
-hipError_t launch_v_tiles_bf16(TileLayout layout, const KeySrc& v, void* vt, int nseq, int len, int H,
-                               hipStream_t stream) {
+hipError_t launch_v_tiles_bf16(const KeySrc& v, void* vt, int nseq, int len, int H, hipStream_t stream) {
   if (nseq <= 0 || len <= 0) return hipSuccess;
   const int ntile = (len + 63) / 64;
-  const dim3 grid((unsigned)ntile, (unsigned)H, (unsigned)nseq);
-  if (layout == kTiles16)
-    hipLaunchKernelGGL(v_tiles_kernel<kTiles16>, grid, dim3(NT), 0, stream, v, (u32x4*)vt, len, H, 0, ntile);
-  else
-    hipLaunchKernelGGL(v_tiles_kernel<kTiles32>, grid, dim3(NT), 0, stream, v, (u32x4*)vt, len, H, 0, ntile);
+  hipLaunchKernelGGL(v_tiles_kernel, dim3((unsigned)ntile, (unsigned)H, (unsigned)nseq), dim3(NT), 0, stream, v,
+                     (u32x4*)vt, len, H, 0, ntile);
   return hipGetLastError();
 }
 
@@ -260,12 +243,12 @@ hipError_t launch_tiles_append_bf16(const void* k, const void* v, void* kt, void
                                     int H, hipStream_t stream) {
   if (n <= 0) return hipSuccess;
   const int tiles = (key0 + n - 1) / 64 - key0 / 64 + 1;
-  hipLaunchKernelGGL(k_tiles_kernel<kTiles16>, dim3((unsigned)tiles, (unsigned)H, 1u), dim3(NT), 0, stream,
+  hipLaunchKernelGGL(k_tiles_kernel, dim3((unsigned)tiles, (unsigned)H, 1u), dim3(NT), 0, stream,
                      contiguous_keys(k, n), (u32x4*)kt, n, H, (const f32x2*)nullptr, 1, key0, dst_ntile,
                      (const float*)nullptr, (const float*)nullptr, 0.0f, 1.0f);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(v_tiles_kernel<kTiles16>, dim3((unsigned)tiles, (unsigned)H, 1u), dim3(NT), 0, stream,
+  hipLaunchKernelGGL(v_tiles_kernel, dim3((unsigned)tiles, (unsigned)H, 1u), dim3(NT), 0, stream,
                      contiguous_keys(v, n), (u32x4*)vt, n, H, key0, dst_ntile);
   return hipGetLastError();
 }
