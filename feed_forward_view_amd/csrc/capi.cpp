@@ -97,19 +97,26 @@ SplitPlan plan_splits(int64_t nq, int64_t nk, int H, int requested, vggt_dtype d
   if (requested > 0) {
     splits = requested;
   } else if (nk > 0 && nq > 0) {
-    // Balance the last wave of workgroups against the merge pass.  Time is
-    // modelled in units of one key tile processed by one resident workgroup:
-    //   attention(s) = ceil(wg * s / slots) * ceil(ktiles / s)
+    // Balance the last round of workgroups against the merge pass.  Time is
+    // modelled in units of one key tile processed by one resident workgroup.
+    // Workgroups run in rounds of `slots`; a last round at most half full runs
+    // one workgroup per CU, which finishes in about half a round, while a
+    // fuller one still pairs workgroups on some CUs and takes a whole round
+    // (measured over global attention at 6 to 40 frames of 1374 tokens):
+    //   attention(s) = ceil(ktiles / s) * (full rounds + tail)
     //   merge(s)     = partial bytes / (bytes one slot-tile-time moves), s > 1
     const int64_t wg = ((nq + query_tile(dt) - 1) / query_tile(dt)) * H;
     const int64_t slots = (int64_t)kAssumedCUs * kWorkgroupsPerCU;
     double best = 1e300;
     for (int s = 1; s <= kMaxSplits && s <= ktiles; ++s) {
-      const double att = (double)((wg * s + slots - 1) / slots) * (double)((ktiles + s - 1) / s);
-      // one tile-time ~ 0.7 us; merge moves s*nq*H*(64+2)*4 bytes twice plus
-      // the output, at ~4 TB/s -> bytes / (4e6 B/us) / 0.7 us
+      const double rounds = (double)(wg * s) / (double)slots;
+      const double full = std::floor(rounds), part = rounds - full;
+      const double tail = part <= 0.0 ? 0.0 : (part <= 0.5 ? 0.5 : 1.0);
+      const double att = (double)((ktiles + s - 1) / s) * (full + tail);
+      // one tile-time ~ 1.8 us; merge moves s*nq*H*(64+2)*4 bytes twice plus
+      // the output, at ~5 TB/s -> bytes / (5e6 B/us) / 1.8 us
       const double bytes = s > 1 ? (double)nq * H * (2.0 * s * 66 * 4 + 64 * 2) : 0.0;
-      const double cost = att + bytes / 4.0e6 / 0.7;
+      const double cost = att + bytes / 5.0e6 / 1.8;
       if (cost < best - 1e-9) {
         best = cost;
         splits = s;
