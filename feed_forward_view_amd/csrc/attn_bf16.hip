@@ -6,20 +6,21 @@
 // against a reference offset, so a row costs O(1) memory for any key count.
 //
 // Work split.  A workgroup of 4 waves (one per SIMD) owns 256 queries of one
-// head; each wave owns 64 of them as four 16-query MFMA column blocks (qb),
-// taken as two halves of 32.  Per 64-key tile and half:
-//   S^T = K Q^T - m   16 x v_mfma_f32_16x16x32_bf16 (4 key blocks of 16 x 2
-//                     channel halves x 2 query blocks); keys are the M
-//                     dimension, so lane l holds 4 scores (keys 16kb + 4(l/16)
-//                     + 0..3) of query l % 16, and the row reference m enters
-//                     through the accumulator input;
-//   P = 2^(S^T)       one v_exp_f32 per score, rounded to bf16 in pairs; the
-//                     row sum adds the rounded pairs with v_dot2_f32_bf16, so
-//                     it uses exactly the weights of the P V product;
-//   O^T += V^T P^T    16 x v_mfma_f32_16x16x32_bf16 (4 channel blocks x 2
-//                     32-key chunks x 2 query blocks); head dim is M and the
-//                     lane again holds one query, so per-row scaling stays
-//                     in-lane.
+// head; each wave owns 64 of them as four 16-query MFMA column blocks (qb).
+// Per 64-key tile and query block:
+//   S^T = K Q^T       8 x v_mfma_f32_16x16x32_bf16 (4 key blocks of 16 x 2
+//                     channel halves); keys are the M dimension, so lane l
+//                     holds 4 scores (keys 16kb + 4(l/16) + 0..3) of query
+//                     l % 16;
+//   P = 2^(S^T - m)   one v_exp_f32 per score, rounded to bf16 in pairs;
+//   O^T += V^T P^T    8 x v_mfma_f32_16x16x32_bf16 (4 channel blocks x 2
+//                     32-key chunks); head dim is M and the lane again holds
+//                     one query, so per-row scaling stays in-lane;
+//   l += 1 P^T        2 x v_mfma_f32_16x16x32_bf16 with an all-ones A
+//                     operand: the row sum uses exactly the bf16 weights of
+//                     the P V product (a single key returns its V row
+//                     bit-exactly), and every register of the result holds
+//                     the lane's query's sum.
 // Q is rotated (2D RoPE, fp32, from the per-position cos/sin table) and
 // multiplied by scale*log2(e) once in the prologue, so scores come out in log2
 // units.  The score registers of key blocks 2c and 2c+1 are, in order, the
@@ -28,24 +29,27 @@
 // and the V^T tiles store their keys in that order.
 //
 // Why 16x16x32: under sustained load this chip holds its clock with the
-// 16x16x32 shape where the 32x32x16 shape runs into the power limit (same
-// cycles per tile, measured ~8 % more clock at this kernel's MFMA density).
+// 16x16x32 shape where the 32x32x16 shape runs into the power limit.
 //
-// Overlap.  While an MFMA runs, plain VALU work (fma, add, cvt) hides almost
-// completely, from the same wave or the other wave on the SIMD; v_exp_f32 (8
-// clocks per wave instruction) hides about half behind the wave's own MFMAs
-// and fully behind the other wave's; v_dot2_f32_bf16 never overlaps an MFMA.
-// The loop therefore keeps VALU work per tile to one exp per score and one cvt
-// and one dot2 per score pair, and interleaves each half's exponentials with
-// the other half's MFMAs.
+// Issue costs that shape the loop (measured on gfx950).  Plain VALU work and
+// v_exp_f32 hide behind a running MFMA as long as the SIMD's VALU issue
+// budget lasts; with one exponential and half a conversion per score that
+// budget is nearly used up.  v_dot2_f32_bf16 and its VOP3P form do not
+// overlap MFMAs at all: a row sum in dot2 costs as much MFMA-pipe time as an
+// MFMA per instruction, four times the ones x P product above.  The loop is
+// software-pipelined over query blocks so that every block's exponentials run
+// beside sixteen independent MFMAs (see the step schedule below).
 //
-// Softmax reference.  m starts at 0 and stays there while a row's scores stay
-// within 2^32 of it.  The first tile, and any tile whose partial row sum
-// leaves [0, 2^64], takes a slow path that computes the tile maximum, moves m
-// (rescaling O and the running sum exactly by 2^(m_old - m_new), except on
-// the first tile, where both are still zero) and redoes the tile; from then on
-// the wave subtracts m before the exponential.  The final O / l is the same
-// softmax whatever m is.
+// Softmax reference, optimistic.  The first pass keeps m = 0 for every row
+// and checks nothing per tile.  At the end a row is accepted when its sum l
+// lies in [2^-64, 2^100]: then no weight overflowed and the largest is at
+// least 2^-64 / N, far inside the normal range of bf16 and fp32, so the pass
+// computed the same softmax as any other reference up to rounding.  If any row
+// of the workgroup fails (logits in the hundreds, or rows whose scores all lie
+// far below zero), the workgroup reruns its key range exactly: the first tile
+// sets a per-row m, every block's largest score is checked against it, and a
+// slow path moves m (rescaling O and l exactly by 2^(m_old - m_new)) and
+// redoes the block.  The final O / l is the same softmax whatever m is.
 //
 // Operands.  A pre-pass lays K (rotated when RoPE is on) and V^T out in
 // tiles of 64 keys, each tile 8 KiB in exactly the order the LDS tile uses
@@ -81,9 +85,10 @@ constexpr int NT = NW * 64;
 constexpr int QW = 64;            // queries per wave: four 16-query MFMA column blocks
 constexpr int BQ = NW * QW;       // queries per workgroup
 constexpr int NSTAGE = VGGT_ATTN_NSTAGE;  // LDS ring depth (tiles in flight = NSTAGE - 1)
-constexpr float kSumLimit = 18446744073709551616.0f;  // 2^64
-constexpr float kRaise = 32.0f;   // move m when a tile max exceeds it by this
-constexpr float kLow = -64.0f;    // first tile: move m down when the max is below this
+// exact pass: move m when a block's largest score exceeds it by kRaise; on the first tile
+// also when that score lies below kLow
+constexpr float kRaise = 32.0f;
+constexpr float kLow = -64.0f;
 constexpr float kLn2 = 0.693147180559945309f;
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -94,12 +99,8 @@ typedef __attribute__((address_space(3))) void lds_void;
 struct Smem {
   u32x4 k[NSTAGE][BK][8];
   u32x4 vt[NSTAGE][D][8];
+  int redo;  // some row of the optimistic pass is out of range: rerun the workgroup exactly
 };
-
-__device__ __forceinline__ float dot2_acc(uint32_t pk, float acc) {
-  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), one, acc, false);
-}
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -112,23 +113,27 @@ __device__ __forceinline__ void wait_vmcnt() {
   else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
 }
 
-// interleave hint for the scheduler: n x (1 MFMA, v VALU)
-#ifndef VGGT_IL_N
-#define VGGT_IL_N 16
-#endif
-#ifndef VGGT_IL_V
-#define VGGT_IL_V 6
-#endif
-#define VGGT_INTERLEAVE(n, v)                                  \
-  _Pragma("unroll") for (int _i = 0; _i < (n); ++_i) {         \
+// Interleave hints for the scheduler, one per half step: 8 x (1 MFMA, 1 exponential, 1 other
+// VALU op), optionally with one LDS fragment read per MFMA.
+#define VGGT_INTERLEAVE8()                                     \
+  _Pragma("unroll") for (int _i = 0; _i < 8; ++_i) {           \
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         \
-    __builtin_amdgcn_sched_group_barrier(0x002, (v), 0);       \
+    __builtin_amdgcn_sched_group_barrier(0x400, 1, 0);         \
+    __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);         \
+  }
+#define VGGT_INTERLEAVE8_DS()                                  \
+  _Pragma("unroll") for (int _i = 0; _i < 8; ++_i) {           \
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         \
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);         \
+    __builtin_amdgcn_sched_group_barrier(0x400, 1, 0);         \
+    __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);         \
   }
 
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(VGGT_ATTN_WPE, VGGT_ATTN_WPE)))
 void attn_fwd_bf16_kernel(AttnProblem p) {
   __shared__ Smem sm;
   const int tid = threadIdx.x;
+  if (tid == 0) sm.redo = 0;  // read only after the first pass, many barriers later
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int l16 = lane & 15;  // query within a 16-query block
@@ -174,13 +179,15 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
 
   // ---- tile loads: each wave copies two 1 KiB blocks of the K tile and two of the V^T tile
   const int ktile0 = kbeg / BK;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   auto issue = [&](int stage, int tile) {
-    const u32x4* ks = ktg + (int64_t)(ktile0 + tile) * 512 + wave * 128 + lane;
-    const u32x4* vs = vtg + (int64_t)(ktile0 + tile) * 512 + wave * 128 + lane;
+    // wave-uniform base (scalar registers) + the lane's 16-byte unit
+    const u32x4* ks = ktg + (int64_t)(ktile0 + tile) * 512 + wave_u * 128;
+    const u32x4* vs = vtg + (int64_t)(ktile0 + tile) * 512 + wave_u * 128;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      __builtin_amdgcn_global_load_lds((const void*)(ks + 64 * c), (lds_void*)&sm.k[stage][(2 * wave + c) * 8][0], 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(vs + 64 * c), (lds_void*)&sm.vt[stage][(2 * wave + c) * 8][0], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(ks + 64 * c + lane), (lds_void*)&sm.k[stage][(2 * wave_u + c) * 8][0], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(vs + 64 * c + lane), (lds_void*)&sm.vt[stage][(2 * wave_u + c) * 8][0], 16, 0, 0);
     }
   };
 
@@ -264,22 +271,25 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
 
   // ---- running state
   f32x4 o[4][4];  // [qb][db]: O^T rows 16db + 4g + r, column = the lane's query of block qb
-#pragma unroll
-  for (int qb = 0; qb < 4; ++qb)
-#pragma unroll
-    for (int db = 0; db < 4; ++db) o[qb][db] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  float mref[4], lsum[4];  // reference (log2 units) and this lane's partial row sums
-  f32x4 negm[4];           // -m of the lane's query, replicated: accumulator input of S^T
+  f32x4 lrow[4];  // [qb]: row sums (ones x P); all four registers hold the lane's query's sum
+  float mrow[4];  // [qb]: reference m of the lane's query (log2 units)
 #pragma unroll
   for (int qb = 0; qb < 4; ++qb) {
-    mref[qb] = lsum[qb] = 0.0f;
-    negm[qb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int db = 0; db < 4; ++db) o[qb][db] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    lrow[qb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    mrow[qb] = 0.0f;
   }
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
 
-  f32x4 s0[2][4], s1[2][4];  // scores of query blocks (0, 1) and (2, 3): [block][kb], keys 16kb + 4g + r
-  u32x4 p0[2][2], p1[2][2];  // [block][chunk]: bf16 pairs, B operand of P V
-  bf16x8 kf[4][2];           // K fragments of the tile [kb][dc]
-  bf16x8 vf[2][4];           // V^T fragments [chunk][db]
+  // Scores and weights of one query block, double-buffered by step parity: step j reads
+  // s[j & 1] and writes pp[j & 1] while its MFMAs fill s[~j & 1] and read pp[~j & 1].
+  f32x4 s[2][4];     // [buffer][kb]: keys 16kb + 4g + r of the lane's query
+  u32x4 pp[2][2];    // [buffer][chunk]: bf16 pairs, B operand of P V
+  bf16x8 kf[4][2];   // K fragments of one tile [kb][dc]
+  bf16x8 vf[2][4];   // V^T fragments of one tile [chunk][db]
 
   auto read_k = [&](int stage) {
 #pragma unroll
@@ -302,55 +312,58 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
         vf[c][db] = __builtin_bit_cast(bf16x8, sm.vt[stage][d][u ^ col_swz(d)]);
       }
   };
-  // S^T - m for query blocks 2h, 2h+1 (the reference enters as the accumulator input)
-  auto qk = [&](f32x4 (&s)[2][4], int h) {
+  // S^T of query block qb; the two products of a key block are four MFMAs apart
+  auto qk = [&](f32x4 (&sd)[4], int qb) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int dc = 0; dc < 2; ++dc)
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        s[i][kb] = mfma(kf[kb][0], qf[2 * h + i][0], negm[2 * h + i]);
-        s[i][kb] = mfma(kf[kb][1], qf[2 * h + i][1], s[i][kb]);
-      }
+      for (int kb = 0; kb < 4; ++kb)
+        sd[kb] = mfma(kf[kb][dc], qf[qb][dc], dc == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : sd[kb]);
   };
-  auto pv = [&](const u32x4 (&pf)[2][2], int h) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-          o[2 * h + i][db] = mfma(vf[c][db], __builtin_bit_cast(bf16x8, pf[i][c]), o[2 * h + i][db]);
-  };
-  // P = 2^(S - shift) of one query block as the bf16 B operand of P V (S already has m
-  // subtracted, up to `shift`); returns this lane's partial row sum
-  auto soft = [&](const f32x4 (&s)[4], bool sub, float shift, u32x4 (&pf)[2]) -> float {
-    float acc = 0.0f;
+  // O^T += V^T P^T and the row sums += 1 P^T of query block qb
+  auto pv = [&](const u32x4 (&pf)[2], int qb) {
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const f32x4& sb = s[2 * c + (e >> 1)];
-        float a = sb[2 * (e & 1)], b = sb[2 * (e & 1) + 1];
-        if (sub) {
-          a -= shift;
-          b -= shift;
-        }
-        const uint32_t w = pack_bf16x2(__builtin_amdgcn_exp2f(a), __builtin_amdgcn_exp2f(b));
-        pf[c][e] = w;
-        acc = dot2_acc(w, acc);
-      }
-    return acc;
+      for (int db = 0; db < 4; ++db) o[qb][db] = mfma(vf[c][db], __builtin_bit_cast(bf16x8, pf[c]), o[qb][db]);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) lrow[qb] = mfma(ones, __builtin_bit_cast(bf16x8, pf[c]), lrow[qb]);
   };
-  // slow path of one query block: move the reference if needed and redo its exponentials
-  auto slow = [&](const f32x4 (&s)[4], int qb, bool first, u32x4 (&pf)[2]) -> float {
-    float mx = s[0][0];
+  // P = 2^(S - m) of 32-key chunk c of one query block as the bf16 B operand of P V
+  // (GEN: m of the lane's query is subtracted; else m = 0)
+  auto soft_c = [&](const f32x4 (&sc)[4], int c, auto gen_c, float m, u32x4& pf) {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int e = 0; e < 4; ++e) {
+      const f32x4& sb = sc[2 * c + (e >> 1)];
+      float a = sb[2 * (e & 1)], b = sb[2 * (e & 1) + 1];
+      if constexpr (decltype(gen_c)::value) {
+        a -= m;
+        b -= m;
+      }
+      pf[e] = pack_bf16x2(__builtin_amdgcn_exp2f(a), __builtin_amdgcn_exp2f(b));
+    }
+  };
+  // largest of the lane's 16 scores of one query block
+  auto smax = [&](const f32x4 (&sc)[4]) -> float {
+    float mx = fmaxf(fmaxf(sc[0][0], sc[0][1]), sc[0][2]);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    // mx is relative to the current reference
+    for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, sc[i >> 2][i & 3]), sc[(i + 1) >> 2][(i + 1) & 3]);
+    return fmaxf(mx, sc[3][3]);
+  };
+  using yes = std::true_type;
+  using no = std::false_type;
+  // slow path of one query block: move the reference if needed, rescale O and the row sum
+  // exactly, and redo the block's exponentials against the new reference
+  auto slow = [&](const f32x4 (&sc)[4], int qb, bool first, u32x4 (&pf)[2]) {
+    float mx = smax(sc);
+    {
+      // the query's other three lanes are l ^ 16, l ^ 32 and l ^ 48
+      const auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(p16[0]), __uint_as_float(p16[1]));
+      const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(p32[0]), __uint_as_float(p32[1]));
+    }
+    mx -= mrow[qb];  // relative to the current reference
     float delta = 0.0f;
     if (first) {
       if (mx < kLow || mx > kRaise) delta = mx;
@@ -358,28 +371,26 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
       delta = mx;
     }
     if (__any(delta != 0.0f)) {
-      mref[qb] += delta;
+      mrow[qb] += delta;
       if (!first) {
         // before the first tile O and l are still zero: only the reference
         // moves (2^-delta overflows when the first tile moves it far down)
         const float alpha = __builtin_amdgcn_exp2f(-delta);
-        lsum[qb] *= alpha;
+        lrow[qb] *= alpha;
 #pragma unroll
         for (int db = 0; db < 4; ++db) o[qb][db] *= alpha;
       }
-      negm[qb] = f32x4{-mref[qb], -mref[qb], -mref[qb], -mref[qb]};
     }
-    return soft(s, true, delta, pf);
+    soft_c(sc, 0, yes{}, mrow[qb], pf[0]);
+    soft_c(sc, 1, yes{}, mrow[qb], pf[1]);
   };
-  auto mask = [&](f32x4 (&s)[2][4], int kt) {
+  auto mask = [&](f32x4 (&sc)[4], int kt) {
     // lane/register -> key kt + 16kb + 4g + r
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (kt + 16 * kb + 4 * g + r >= kend) s[i][kb][r] = -INFINITY;
+      for (int r = 0; r < 4; ++r)
+        if (kt + 16 * kb + 4 * g + r >= kend) sc[kb][r] = -INFINITY;
   };
 
   // wait until tile `tile` has landed in LDS (later tiles may still be in flight), then barrier
@@ -393,78 +404,144 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
       wait_vmcnt<0>();
     __syncthreads();
   };
+  // tile `tile` lands; the ring slot of tile `tile` - 1 (no wave reads it any more) takes
+  // tile `tile` + NSTAGE - 1
+  auto advance = [&](int tile) {
+    land(tile);
+    if (tile + NSTAGE - 1 < ntiles) issue((tile + NSTAGE - 1) % NSTAGE, tile + NSTAGE - 1);
+  };
 
-  // One tile: S^T of query blocks 2-3 || exponentials of blocks 0-1, then P V of blocks 0-1 ||
-  // exponentials of blocks 2-3.  FIRST: the reference is set by the slow path; LAST: keys past
-  // the end are masked.
-  auto tile_body = [&](int t, auto first_c, auto last_c) {
+  // Software pipeline over steps j = 4t + b (tile t, query block b).  Step j exponentiates
+  // block b's scores of tile t while its MFMAs finish the previous step's block (P V and
+  // row sums) and start the next one (S^T), so the exponentials of a block always run
+  // beside independent MFMAs:
+  //   b = 0:  P V (t-1, 3) | V(t) fragments, S^T (t, 1)
+  //   b = 1:  P V (t, 0)   | S^T (t, 2)
+  //   b = 2:  P V (t, 1)   | S^T (t, 3); then tile t+1 lands and its K fragments are read
+  //   b = 3:  P V (t, 2)   | S^T (t+1, 0)
+  // Each step is two halves, each interleaving its MFMAs with one 32-key chunk of the
+  // block's exponentials.  FIRST: tile 0 (no P V of a previous tile); LAST: keys past the
+  // end are masked and no next tile is touched.
+  // EXACT: the per-row reference m of the exact pass: the first tile sets it, every block's
+  // largest score is checked against it, and the slow path moves it (the exponentials
+  // subtract it).  Otherwise m = 0 throughout and nothing is checked.
+  auto step = [&](int t, auto b_c, auto first_c, auto last_c, auto exact_c) {
+    constexpr int b = decltype(b_c)::value;
     constexpr bool first = decltype(first_c)::value;
-    constexpr bool masked = decltype(last_c)::value;
+    constexpr bool last = decltype(last_c)::value;
+    constexpr bool exact = decltype(exact_c)::value;
+    constexpr int cur = b & 1, nxt = cur ^ 1;
     const int stage = t % NSTAGE;
-    read_k(stage);
-    qk(s0, 0);
-    if constexpr (masked) mask(s0, kbeg + t * BK);
-    qk(s1, 1);
-    float a0 = soft(s0[0], false, 0.0f, p0[0]);
-    float a1 = soft(s0[1], false, 0.0f, p0[1]);
-    VGGT_INTERLEAVE(VGGT_IL_N, VGGT_IL_V);
-    if constexpr (masked) mask(s1, kbeg + t * BK);
-    if (first || __any(!(a0 <= kSumLimit) || !(a1 <= kSumLimit))) {
-      a0 = slow(s0[0], 0, first, p0[0]);
-      a1 = slow(s0[1], 1, first, p0[1]);
+    if constexpr (last) mask(s[cur], kbeg + t * BK);
+    // first half: P V of the previous step's block
+    if constexpr (b == 0) {
+      if constexpr (!first) pv(pp[nxt], 3);
+    } else {
+      pv(pp[nxt], b - 1);
     }
-    lsum[0] += a0;
-    lsum[1] += a1;
-    read_v(stage);
-    pv(p0, 0);
-    float b0 = soft(s1[0], false, 0.0f, p1[0]);
-    float b1 = soft(s1[1], false, 0.0f, p1[1]);
-    VGGT_INTERLEAVE(VGGT_IL_N, VGGT_IL_V);
-    if (first || __any(!(b0 <= kSumLimit) || !(b1 <= kSumLimit))) {
-      b0 = slow(s1[0], 2, first, p1[0]);
-      b1 = slow(s1[1], 3, first, p1[1]);
+    if constexpr (!(exact && first)) {
+      soft_c(s[cur], 0, exact_c, mrow[b], pp[cur][0]);
+      VGGT_INTERLEAVE8();
     }
-    lsum[2] += b0;
-    lsum[3] += b1;
-    pv(p1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    // second half: S^T of the next step's block
+    if constexpr (b == 0) read_v(stage);
+    if constexpr (b < 3) {
+      qk(s[nxt], b + 1);
+    } else if constexpr (!last) {
+      qk(s[nxt], 0);
+    }
+    if constexpr (exact && first) {
+      slow(s[cur], b, true, pp[cur]);
+    } else {
+      soft_c(s[cur], 1, exact_c, mrow[b], pp[cur][1]);
+      if constexpr (b == 0) {
+        VGGT_INTERLEAVE8_DS();
+      } else {
+        VGGT_INTERLEAVE8();
+      }
+      if constexpr (exact) {
+        if (__any(smax(s[cur]) - mrow[b] > kRaise)) slow(s[cur], b, false, pp[cur]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (b == 2 && !last) {
+      advance(t + 1);
+      read_k((t + 1) % NSTAGE);
+    }
   };
-  using yes = std::true_type;
-  using no = std::false_type;
-  auto advance = [&](int t) {
-    land(t);
-    if (t + NSTAGE - 1 < ntiles) issue((t + NSTAGE - 1) % NSTAGE, t + NSTAGE - 1);
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  using B2 = std::integral_constant<int, 2>;
+  using B3 = std::integral_constant<int, 3>;
+  auto tile = [&](int t, auto first_c, auto last_c, auto exact_c) {
+    step(t, B0{}, first_c, last_c, exact_c);
+    step(t, B1{}, first_c, last_c, exact_c);
+    step(t, B2{}, first_c, last_c, exact_c);
+    step(t, B3{}, first_c, last_c, exact_c);
+  };
+  // one pass over the key range (the first NSTAGE - 1 tiles are already issued)
+  auto pass = [&](auto exact_c) {
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[qb][db] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      lrow[qb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      mrow[qb] = 0.0f;
+    }
+    advance(0);
+    read_k(0);
+    qk(s[0], 0);
+    if (ntiles == 1) {
+      tile(0, yes{}, yes{}, exact_c);
+    } else {
+      tile(0, yes{}, no{}, exact_c);
+      for (int t = 1; t + 1 < ntiles; ++t) tile(t, no{}, no{}, exact_c);
+      tile(ntiles - 1, no{}, yes{}, exact_c);
+    }
+    pv(pp[1], 3);
   };
 
+  // Optimistic pass: m = 0 for every row, so 2^s must neither overflow nor vanish.  A row
+  // whose sum lies in [2^-64, 2^100] had every weight finite and its largest weight at
+  // least 2^-64 / N, which bf16 and fp32 hold at full precision, so the pass is exact up to
+  // rounding.  Otherwise the whole workgroup (its barrier and copy sequence is shared)
+  // reruns the key range with the exact per-row reference.
   if (active) {
-    if (ntiles == 1) {
-      advance(0);
-      tile_body(0, yes{}, yes{});
-    } else {
-      advance(0);
-      tile_body(0, yes{}, no{});
-      for (int t = 1; t + 1 < ntiles; ++t) {
-        advance(t);
-        tile_body(t, no{}, no{});
-      }
-      advance(ntiles - 1);
-      tile_body(ntiles - 1, no{}, yes{});
+    pass(no{});
+    bool bad = false;
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) {
+      const float l = lrow[qb][0];
+      if (q0 + 16 * qb + l16 < nq_seq && !(l >= 0x1p-64f && l <= 0x1p100f)) bad = true;
     }
+    if (__any(bad) && lane == 0) sm.redo = 1;
   } else {
     // keep the workgroup's barrier and load sequence
     for (int t = 0; t < ntiles; ++t) advance(t);
-    return;
   }
+  __syncthreads();
+  if (sm.redo) {
+#pragma unroll
+    for (int i = 0; i < NSTAGE - 1; ++i)
+      if (i < ntiles) issue(i, i);
+    if (active) {
+      pass(yes{});
+    } else {
+      for (int t = 0; t < ntiles; ++t) advance(t);
+    }
+  }
+  if (!active) return;
 
   // ---- epilogue: the 4 lanes of a query (g = 0..3) hold its 64 channels, 16 each
 #pragma unroll
   for (int qb = 0; qb < 4; ++qb) {
-    float ltot = lsum[qb] + __shfl_xor(lsum[qb], 16);
-    ltot += __shfl_xor(ltot, 32);
+    const float ltot = lrow[qb][0];
     const int qi = q0 + 16 * qb + l16;
     if (qi >= nq_seq) continue;
     if (p.splits == 1) {
       const float inv = 1.0f / ltot;
-      if (p.lse && g == 0) p.lse[(seq * p.q_seq_stride + qi) * p.H + head] = (mref[qb] + log2f(ltot)) * kLn2;
+      if (p.lse && g == 0) p.lse[(seq * p.q_seq_stride + qi) * p.H + head] = (mrow[qb] + log2f(ltot)) * kLn2;
       uint16_t* og = (uint16_t*)p.o + (seq * p.q_seq_stride + qi) * p.tok_stride + head * D;
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
@@ -478,7 +555,7 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
 #pragma unroll
       for (int db = 0; db < 4; ++db) *(f32x4*)(po + 16 * db + 4 * g) = o[qb][db];
       if (g == 0) {
-        const f32x2 ml = {mref[qb], ltot};
+        const f32x2 ml = {mrow[qb], ltot};
         *(f32x2*)(p.part_ml + row * 2) = ml;
       }
     }

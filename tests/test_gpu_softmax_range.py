@@ -9,12 +9,16 @@ units of zero, so they never exercise three exact paths of the online softmax
   reference during the key loop and the running O and l are rescaled;
 * rows whose scores all lie far below zero, so the first tile moves the
   reference down and the log-normaliser is far below zero;
-* a row maximum that first appears in a late (or the last, masked) key tile,
-  so the per-tile partial-sum check sends that tile to the exact slow path.
+* a row maximum that first appears in a late (or the last, masked) key tile;
+* only some rows sharp (one frame's queries scaled up), so some workgroups
+  rerun exactly and others keep their optimistic result, and split partials
+  with and without a reference are merged;
+* frames whose row sums sit just inside and just outside the optimistic
+  pass's acceptance bound, so results from both sides of it are compared.
 
 Split launches then merge partials whose references differ by hundreds.
 
-The scale is 8 ln 2 (or ln 2 / 8 for the offset case), which makes
+The scale is 8 ln 2 (or ln 2 / 8 for the offset, mixed and edge cases), which makes
 scale * log2(e) = 8 (1/8) to within a float32 ulp.  The kernels' scaled bf16
 query operand is then exact, and the comparison sees only the softmax
 arithmetic.  Bars:
@@ -45,7 +49,8 @@ pytestmark = pytest.mark.gpu
 
 SHARP = float(np.float32(8.0 * np.log(2.0)))
 MILD = float(np.float32(np.log(2.0) / 8.0))
-KINDS = ["sharp", "negative", "late", "offset"]
+KINDS = ["sharp", "negative", "late", "offset", "mixed", "edge"]
+MILD_KINDS = ("offset", "mixed", "edge")
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -78,6 +83,21 @@ def _case(kind, dtype):
         qf[..., 63] = 256.0
         kf[..., 63] = -12.0
         q, k = workload.f32_to_bf16_bits(qf), workload.f32_to_bf16_bits(kf)
+    elif kind == "mixed":
+        # frame 1's queries x 64: their scores spread over hundreds of log2 units
+        qf = workload.bf16_bits_to_f32(q)
+        qf[1] *= 64.0
+        q = workload.f32_to_bf16_bits(qf)
+    elif kind == "edge":
+        # channel 63: query 31, 35, 37 in frames 0, 1, 2 and key -16, so frame
+        # f's scores sit near -62, -70, -74 log2 units and its frame-attention
+        # row sums near 2^-55, 2^-63.2 and 2^-67.3: frame 1 is just inside the
+        # optimistic pass's bound (2^-64), frame 2 just outside
+        qf, kf = workload.bf16_bits_to_f32(q), workload.bf16_bits_to_f32(k)
+        for f, c in enumerate((31.0, 35.0, 37.0)):
+            qf[f, :, :, 63] = c
+        kf[..., 63] = -16.0
+        q, k = workload.f32_to_bf16_bits(qf), workload.f32_to_bf16_bits(kf)
     elif kind == "late":
         # key 70 of frame 2 (global key 242, in the fourth of five key tiles;
         # frame-local key 70 is in the last, masked tile) gets 4x the scores
@@ -86,7 +106,7 @@ def _case(kind, dtype):
         k = workload.f32_to_bf16_bits(kf)
     if dtype == torch.float32:
         q, k, v = (workload.bf16_bits_to_f32(x) for x in (q, k, v))
-    scale = MILD if kind == "offset" else SHARP
+    scale = MILD if kind in MILD_KINDS else SHARP
     return wl, q, k, v, scale
 
 
@@ -135,7 +155,7 @@ def test_softmax_range_forward(kind, dtype):
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-@pytest.mark.parametrize("kind", ["sharp", "late", "offset"])
+@pytest.mark.parametrize("kind", ["sharp", "late", "offset", "mixed"])
 def test_softmax_range_backward(kind, dtype):
     wl, q, k, v, SCALE = _case(kind, dtype)
     S, T, H = wl.S, wl.T, wl.H
