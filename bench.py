@@ -38,9 +38,9 @@ PEAK_HBM_GBS = 8000.0
 # plain 1 GiB copy (profiles/attn_fwd_bf16_vggt-518-s32_counters.md).  Valid
 # only for the kernel source it was measured on.
 PROFILED_TRAFFIC = {
-    "kernel_source_sha256": "aeb10522fdeaaa7d44125fffccff9bd8625b4b73d848c4d447e5baf35a2b3c79",
-    "read_bytes": 1344.4e6,
-    "write_bytes": 405.2e6,
+    "kernel_source_sha256": "76657c8a0e6b3785ef5b8289e65a7209354053455ef61935c0061f819aa041f6",
+    "read_bytes": 1177.8e6,
+    "write_bytes": 90.0e6,
 }
 
 

@@ -403,6 +403,9 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
     else
       wait_vmcnt<0>();
     __syncthreads();
+    // the copies wrote LDS behind the compiler's back: no LDS value read before this point
+    // may stand in for a read after it
+    asm volatile("" ::: "memory");
   };
   // tile `tile` lands; the ring slot of tile `tile` - 1 (no wave reads it any more) takes
   // tile `tile` + NSTAGE - 1
@@ -425,14 +428,15 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
   // EXACT: the per-row reference m of the exact pass: the first tile sets it, every block's
   // largest score is checked against it, and the slow path moves it (the exponentials
   // subtract it).  Otherwise m = 0 throughout and nothing is checked.
+  // (the first tile takes LAST at run time: a key range of one tile)
   auto step = [&](int t, auto b_c, auto first_c, auto last_c, auto exact_c) {
     constexpr int b = decltype(b_c)::value;
     constexpr bool first = decltype(first_c)::value;
-    constexpr bool last = decltype(last_c)::value;
     constexpr bool exact = decltype(exact_c)::value;
+    const bool last = first ? ntiles == 1 : decltype(last_c)::value;
     constexpr int cur = b & 1, nxt = cur ^ 1;
     const int stage = t % NSTAGE;
-    if constexpr (last) mask(s[cur], kbeg + t * BK);
+    if (last) mask(s[cur], kbeg + t * BK);
     // first half: P V of the previous step's block
     if constexpr (b == 0) {
       if constexpr (!first) pv(pp[nxt], 3);
@@ -448,7 +452,7 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
     if constexpr (b == 0) read_v(stage);
     if constexpr (b < 3) {
       qk(s[nxt], b + 1);
-    } else if constexpr (!last) {
+    } else if (!last) {
       qk(s[nxt], 0);
     }
     if constexpr (exact && first) {
@@ -465,9 +469,11 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (b == 2 && !last) {
-      advance(t + 1);
-      read_k((t + 1) % NSTAGE);
+    if constexpr (b == 2) {
+      if (!last) {
+        advance(t + 1);
+        read_k((t + 1) % NSTAGE);
+      }
     }
   };
   using B0 = std::integral_constant<int, 0>;
@@ -492,13 +498,9 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
     advance(0);
     read_k(0);
     qk(s[0], 0);
-    if (ntiles == 1) {
-      tile(0, yes{}, yes{}, exact_c);
-    } else {
-      tile(0, yes{}, no{}, exact_c);
-      for (int t = 1; t + 1 < ntiles; ++t) tile(t, no{}, no{}, exact_c);
-      tile(ntiles - 1, no{}, yes{}, exact_c);
-    }
+    tile(0, yes{}, no{}, exact_c);
+    for (int t = 1; t + 1 < ntiles; ++t) tile(t, no{}, no{}, exact_c);
+    if (ntiles > 1) tile(ntiles - 1, no{}, yes{}, exact_c);
     pv(pp[1], 3);
   };
 
