@@ -393,7 +393,10 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
         if (kt + 16 * kb + 4 * g + r >= kend) sc[kb][r] = -INFINITY;
   };
 
-  // wait until tile `tile` has landed in LDS (later tiles may still be in flight), then barrier
+  // wait until tile `tile` has landed in LDS (later tiles may still be in flight), then
+  // barrier: each wave's counter wait covers its own copies of the tile and the barrier
+  // covers every wave's, so the barrier itself waits for nothing else (a __syncthreads
+  // would also drain the copies of later tiles)
   auto land = [&](int tile) {
     const int ahead = min(NSTAGE - 2, ntiles - 1 - tile);  // tiles issued after `tile`
     if (ahead >= 2)
@@ -402,7 +405,7 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
       wait_vmcnt<4>();
     else
       wait_vmcnt<0>();
-    __syncthreads();
+    __builtin_amdgcn_s_barrier();
     // the copies wrote LDS behind the compiler's back: no LDS value read before this point
     // may stand in for a read after it
     asm volatile("" ::: "memory");
