@@ -57,6 +57,15 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 w) { return __builtin_bit_cast(bf16x8, w); }
 
+// Workgroup barrier for the tile ring.  __syncthreads() would make the compiler drain every
+// outstanding copy first, including the next tile's, which was issued just before; the
+// explicit counter waits already cover the copies each barrier needs.  The empty asm keeps
+// LDS reads from being moved or merged across it (the copies write LDS unseen).
+__device__ __forceinline__ void tile_barrier() {
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -165,13 +174,13 @@ void attn_bwd_dq_kernel(AttnBwdProblem p) {
   for (int t = 0; t < p.ntile; ++t) {
     const int stage = t & 1;
     if (t + 1 < p.ntile) {
-      __syncthreads();  // every wave is done with the stage tile t+1 goes to
+      tile_barrier();  // every wave is done with the stage tile t+1 goes to
       issue(stage ^ 1, t + 1);
-      wait_vmcnt<6>();
+      wait_vmcnt<6>();  // tile t has landed (tile t+1 may still be in flight)
     } else {
       wait_vmcnt<0>();
     }
-    __syncthreads();
+    tile_barrier();  // ... in every wave's copies
     bf16x8 kf[4][2], vf[4][2], ktf[2][4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -321,13 +330,13 @@ void attn_bwd_dkdv_kernel(AttnBwdProblem p) {
   for (int t = 0; t < p.ntile; ++t) {
     const int stage = t & 1;
     if (t + 1 < p.ntile) {
-      __syncthreads();
+      tile_barrier();  // every wave is done with the stage tile t+1 goes to
       issue(stage ^ 1, t + 1);
-      wait_vmcnt<9>();
+      wait_vmcnt<9>();  // tile t has landed (tile t+1 may still be in flight)
     } else {
       wait_vmcnt<0>();
     }
-    __syncthreads();
+    tile_barrier();  // ... in every wave's copies
     // the tile's 64 queries as two 32-query chunks c, each two 16-query blocks
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
