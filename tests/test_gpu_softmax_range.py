@@ -177,3 +177,37 @@ def test_softmax_range_backward(kind, dtype):
             check_grad(to_f64(got), ref, f"{tag} {name}", True)
         else:
             _check_f32(to_f64(got), ref, f"{tag} {name}", smax)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("kind", ["sharp", "negative", "plain"])
+def test_single_tile_key_range(kind, dtype):
+    """Key ranges of one 64-key tile (frames of 7 x 7 patches + 5 special = 54 tokens;
+    global attention over one frame): the first tile is also the last, in the optimistic
+    pass and, for the sharp and all-negative rows, in the exact rerun."""
+    wl = workload.Workload("t", 73, S=2, gh=7, gw=7, n_special=5, patch_begin=5, H=2)
+    q, k, v = wl.qkv_bf16()
+    if kind == "negative":
+        q = q & np.uint16(0x7FFF)
+        k = k | np.uint16(0x8000)
+    scale = SHARP if kind != "plain" else float(np.float32(0.125))
+    bf16 = dtype == torch.bfloat16
+    if not bf16:
+        q, k, v = (workload.bf16_bits_to_f32(x) for x in (q, k, v))
+    S, T = wl.S, wl.T
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    tag = f"{kind} {'bf16' if bf16 else 'f32'}"
+    fo = ffv.vggt_frame_attn(qd, kd, vd, scale=scale)
+    ref = oracle.frame_attn(q, k, v, S, T, scale=scale)
+    if bf16:
+        check_bf16(to_f64(fo), ref, f"frame one tile {tag}")
+    else:
+        _check_f32(to_f64(fo), ref, f"frame one tile {tag}", _score_bound(q, k, S, T, False, scale))
+    # one frame as the global sequence: N = 54 keys, one tile
+    q1, k1, v1 = q[:1], k[:1], v[:1]
+    go = ffv.vggt_global_attn(to_dev(q1), to_dev(k1), to_dev(v1), scale=scale)
+    ref = oracle.global_attn(q1, k1, v1, 1, T, scale=scale)
+    if bf16:
+        check_bf16(to_f64(go), ref, f"global one tile {tag}")
+    else:
+        _check_f32(to_f64(go), ref, f"global one tile {tag}", _score_bound(q1, k1, 1, T, True, scale))
