@@ -43,6 +43,13 @@
  *     or touching the device, and the workspace queries return 0.  The one
  *     exception is vggt_global_attn_ex with n_extra > 0 and S = 0, which is
  *     VGGT_ERR_SHAPE.
+ *   - Running time (bf16 forward calls): the kernel first computes every
+ *     row's softmax against a fixed reference and checks each row's sum at
+ *     the end.  A workgroup with a row outside the range recomputes its 256
+ *     rows exactly, taking up to about 2.4x the usual time.  Such a row has a
+ *     largest logit above about 50 or all logits below about -40 (natural
+ *     units, scale included).  Results are the same softmax either way, up to
+ *     rounding.
  */
 #ifndef VGGT_ATTN_H
 #define VGGT_ATTN_H
