@@ -144,3 +144,36 @@ def test_kernel_timer_brackets_attention_kernels():
     ffv.vggt_frame_attn(qd, kd, vd)
     ffv.vggt_frame_attn(qd, kd, vd)
     assert [kind for kind, _ in ffv.vggt_timer_stop()] == ["frame"]
+
+
+@pytest.mark.parametrize("kind", ["sharp", "negative"])
+def test_stream_softmax_range(kind):
+    """Cache attention (per chunk, split and unsplit), the one-launch chunked form and the
+    full cross-attention on rows whose softmax leaves the optimistic pass's range: logits
+    in the hundreds (scale 8 ln 2) or all far below zero (q >= 0 >= k), so workgroups rerun
+    their key ranges exactly, with per-sequence key prefixes and a shared key set.  The
+    descriptors are seeded bf16 values given directly (41 per frame, ragged against the
+    64-key tiles), so both sides start from identical inputs."""
+    S, F, H, T, Dn = 5, 2, 2, 86, 41
+    q = workload.normal_bf16(0x5A0, (S, T, H, 64))
+    kp = workload.normal_bf16(0x5A1, (S, Dn, H, 64))
+    vp = workload.normal_bf16(0x5A2, (S, Dn, H, 64))
+    if kind == "negative":
+        q = q & np.uint16(0x7FFF)
+        kp = kp | np.uint16(0x8000)
+    scale = float(np.float32(8.0 * np.log(2.0)))
+    qd, kpd, vpd = to_dev(q), to_dev(kp), to_dev(vp)
+    ref = oracle.descriptor_stream_xattn(q, kp, vp, F, scale=scale).reshape(S, T, H, 64)
+    cache = _nan_cache(S * Dn, H, torch.bfloat16)
+    for c in range((S + F - 1) // F):
+        f0, f1 = c * F, min(S, (c + 1) * F)
+        cache.append(kpd[f0:f1], vpd[f0:f1])
+        for splits in (1, 3, 0):
+            o = cache.attend(qd[f0:f1], scale=scale, kv_splits=splits)
+            check_bf16(to_f64(o), ref[f0:f1], f"{kind} stream chunk {c} splits={splits}")
+    check_bf16(to_f64(cache.attend_chunked(qd, Dn, F, scale=scale)), ref, f"{kind} chunked one launch")
+    xref = oracle.attention(q.reshape(S * T, H, 64), kp.reshape(S * Dn, H, 64), vp.reshape(S * Dn, H, 64),
+                            scale=scale)
+    for splits in (1, 2):
+        x = ffv.vggt_descriptor_xattn(qd, kpd, vpd, scale=scale, kv_splits=splits)
+        check_bf16(to_f64(x), xref.reshape(S, T, H, 64), f"{kind} descriptor xattn splits={splits}")
