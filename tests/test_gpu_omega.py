@@ -105,3 +105,26 @@ def test_omega_full_size():
     fo = ffv.vggt_frame_attn_ex(qd, kd, vd, Ta, pos_yx=pd)
     fr = oracle.frame_attn(q[:, :Ta], k[:, :Ta], v[:, :Ta], S, Ta, pos=pos[:Ta], rows=rows)
     check_bf16(to_f64(fo[:, :Ta].contiguous()).reshape(n, H, 64)[rows], fr, f"s64 frame_ex ({rows.size} rows)")
+
+
+def test_omega_softmax_range():
+    """The Omega forms (registers left out, extra sequence-level tokens) on logits in the
+    hundreds (scale 8 ln 2), so their workgroups rerun their key ranges exactly.  No RoPE
+    or LayerNorm: at this scale the bf16 rounding of rotated or normalised operands, which
+    the float64 oracle does not share, would move the weights by far more than the bar.
+    With scale * log2(e) = 8 the kernels' operands are exact."""
+    wl = workload.Workload("t", 53, S=3, gh=6, gw=6, n_special=4, patch_begin=0, H=2)
+    S, T, H, Ta, E = wl.S, wl.T, wl.H, 36, 3
+    q, k, v = wl.qkv_bf16()
+    xq, xk, xv = _extras(0xE77B, E, H, torch.bfloat16)
+    scale = float(np.float32(8.0 * np.log(2.0)))
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    xqd, xkd, xvd = to_dev(xq), to_dev(xk), to_dev(xv)
+    fo = ffv.vggt_frame_attn_ex(qd, kd, vd, Ta, scale=scale)
+    ref = oracle.frame_attn_ex(q, k, v, S, T, Ta, scale=scale)
+    check_bf16(to_f64(fo)[:, :Ta], ref, "sharp frame_ex")
+    rf, rx = oracle.global_attn_ex(q, k, v, S, T, Ta, xq, xk, xv, scale=scale)
+    for splits in (1, 3):
+        go, xo = ffv.vggt_global_attn_ex(qd, kd, vd, Ta, xqd, xkd, xvd, scale=scale, kv_splits=splits)
+        check_bf16(to_f64(go)[:, :Ta], rf, f"sharp global_ex frames splits={splits}")
+        check_bf16(to_f64(xo), rx, f"sharp global_ex extras splits={splits}")
