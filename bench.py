@@ -38,7 +38,7 @@ PEAK_HBM_GBS = 8000.0
 # plain 1 GiB copy (profiles/attn_fwd_bf16_vggt-518-s32_counters.md).  Valid
 # only for the kernel source it was measured on.
 PROFILED_TRAFFIC = {
-    "kernel_source_sha256": "a9c0643c4ad461ac7252b8be55b83a23ec614d9a98289d3eac08054c08e862ee",
+    "kernel_source_sha256": "d4938237c5623d4951033f0fff14e2e96a41ffc15ee3d6eb912464e3bb2ada3a",
     "read_bytes": 1175.6e6,
     "write_bytes": 90.0e6,
 }

@@ -82,7 +82,11 @@ constexpr int NW = 4;             // waves per workgroup
 #define VGGT_ATTN_WPE 2
 #endif
 constexpr int NT = NW * 64;
-constexpr int QW = 64;            // queries per wave: four 16-query MFMA column blocks
+#ifndef VGGT_ATTN_NQB
+#define VGGT_ATTN_NQB 4
+#endif
+constexpr int NQB = VGGT_ATTN_NQB;  // 16-query MFMA column blocks per wave
+constexpr int QW = 16 * NQB;        // queries per wave
 constexpr int BQ = NW * QW;       // queries per workgroup
 constexpr int NSTAGE = VGGT_ATTN_NSTAGE;  // LDS ring depth (tiles in flight = NSTAGE - 1)
 // exact pass: move m when a block's largest score exceeds it by kRaise; on the first tile
@@ -111,6 +115,15 @@ __device__ __forceinline__ void wait_vmcnt() {
   if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
   else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+}
+
+// f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
 }
 
 // Interleave hints for the scheduler, one per half step: 8 x (1 MFMA, 1 exponential, 1 other
@@ -198,11 +211,11 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
   // ---- Q fragments (B operand of S^T = K Q^T): lane holds query q0 + 16qb + l16,
   //      channels 32dc + 8g .. +7 (the other 48 sit in the lanes of the same l16),
   //      after an optional per-head LayerNorm, rotated and scaled by scale*log2(e).
-  bf16x8 qf[4][2];
+  bf16x8 qf[NQB][2];
   {
     const f32x2* __restrict__ tab = p.rope_tab;
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
+    for (int qb = 0; qb < NQB; ++qb) {
       const int qi = q0 + 16 * qb + l16;
       const bool ok = qi < nq_seq;
       const int qrow = ok ? qi : 0;
@@ -270,11 +283,11 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
   }
 
   // ---- running state
-  f32x4 o[4][4];  // [qb][db]: O^T rows 16db + 4g + r, column = the lane's query of block qb
-  f32x4 lrow[4];  // [qb]: row sums (ones x P); all four registers hold the lane's query's sum
-  float mrow[4];  // [qb]: reference m of the lane's query (log2 units)
+  f32x4 o[NQB][4];  // [qb][db]: O^T rows 16db + 4g + r, column = the lane's query of block qb
+  f32x4 lrow[NQB];  // [qb]: row sums (ones x P); all four registers hold the lane's query's sum
+  float mrow[NQB];  // [qb]: reference m of the lane's query (log2 units)
 #pragma unroll
-  for (int qb = 0; qb < 4; ++qb) {
+  for (int qb = 0; qb < NQB; ++qb) {
 #pragma unroll
     for (int db = 0; db < 4; ++db) o[qb][db] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     lrow[qb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -417,7 +430,7 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
     if (tile + NSTAGE - 1 < ntiles) issue((tile + NSTAGE - 1) % NSTAGE, tile + NSTAGE - 1);
   };
 
-  // Software pipeline over steps j = 4t + b (tile t, query block b).  Step j exponentiates
+  // Software pipeline over steps j = NQB t + b (tile t, query block b; shown for NQB = 4).  Step j exponentiates
   // block b's scores of tile t while its MFMAs finish the previous step's block (P V and
   // row sums) and start the next one (S^T), so the exponentials of a block always run
   // beside independent MFMAs:
@@ -442,7 +455,7 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
     if (last) mask(s[cur], kbeg + t * BK);
     // first half: P V of the previous step's block
     if constexpr (b == 0) {
-      if constexpr (!first) pv(pp[nxt], 3);
+      if constexpr (!first) pv(pp[nxt], NQB - 1);
     } else {
       pv(pp[nxt], b - 1);
     }
@@ -453,7 +466,7 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
     __builtin_amdgcn_sched_barrier(0);
     // second half: S^T of the next step's block
     if constexpr (b == 0) read_v(stage);
-    if constexpr (b < 3) {
+    if constexpr (b < NQB - 1) {
       qk(s[nxt], b + 1);
     } else if (!last) {
       qk(s[nxt], 0);
@@ -472,27 +485,20 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (b == 2) {
+    if constexpr (b == NQB - 2) {
       if (!last) {
         advance(t + 1);
         read_k((t + 1) % NSTAGE);
       }
     }
   };
-  using B0 = std::integral_constant<int, 0>;
-  using B1 = std::integral_constant<int, 1>;
-  using B2 = std::integral_constant<int, 2>;
-  using B3 = std::integral_constant<int, 3>;
   auto tile = [&](int t, auto first_c, auto last_c, auto exact_c) {
-    step(t, B0{}, first_c, last_c, exact_c);
-    step(t, B1{}, first_c, last_c, exact_c);
-    step(t, B2{}, first_c, last_c, exact_c);
-    step(t, B3{}, first_c, last_c, exact_c);
+    static_for<0, NQB>([&](auto b_c) { step(t, b_c, first_c, last_c, exact_c); });
   };
   // one pass over the key range (the first NSTAGE - 1 tiles are already issued)
   auto pass = [&](auto exact_c) {
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
+    for (int qb = 0; qb < NQB; ++qb) {
 #pragma unroll
       for (int db = 0; db < 4; ++db) o[qb][db] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       lrow[qb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -504,7 +510,7 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
     tile(0, yes{}, no{}, exact_c);
     for (int t = 1; t + 1 < ntiles; ++t) tile(t, no{}, no{}, exact_c);
     if (ntiles > 1) tile(ntiles - 1, no{}, yes{}, exact_c);
-    pv(pp[1], 3);
+    pv(pp[(NQB - 1) & 1], NQB - 1);
   };
 
   // Optimistic pass: m = 0 for every row, so 2^s must neither overflow nor vanish.  A row
@@ -516,7 +522,7 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
     pass(no{});
     bool bad = false;
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
+    for (int qb = 0; qb < NQB; ++qb) {
       const float l = lrow[qb][0];
       if (q0 + 16 * qb + l16 < nq_seq && !(l >= 0x1p-64f && l <= 0x1p100f)) bad = true;
     }
@@ -540,7 +546,7 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
 
   // ---- epilogue: the 4 lanes of a query (g = 0..3) hold its 64 channels, 16 each
 #pragma unroll
-  for (int qb = 0; qb < 4; ++qb) {
+  for (int qb = 0; qb < NQB; ++qb) {
     const float ltot = lrow[qb][0];
     const int qi = q0 + 16 * qb + l16;
     if (qi >= nq_seq) continue;
@@ -570,6 +576,7 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
 }  // namespace
 
 int attn_bf16_query_tile() { return BQ; }
+int attn_bf16_workgroups_per_cu() { return VGGT_ATTN_WPE; }
 
 hipError_t launch_attn_bf16(const AttnProblem& p, hipStream_t stream) {
   const int ntq = (p.nq + BQ - 1) / BQ;

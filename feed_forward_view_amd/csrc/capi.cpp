@@ -33,10 +33,6 @@ constexpr int kMaxHeads = 128;
 constexpr int64_t kMaxTokens = int64_t(1) << 28;
 constexpr int kMaxSplits = 64;
 constexpr int kAssumedCUs = 256;       // MI355X; used only to size the key split
-#ifndef VGGT_ATTN_WPE
-#define VGGT_ATTN_WPE 2
-#endif
-constexpr int kWorkgroupsPerCU = VGGT_ATTN_WPE;  // the bf16 kernel's 4-wave workgroups resident per CU
 
 // ---- device check, cached per device (read-only after first use)
 struct DevInfo {
@@ -106,7 +102,7 @@ SplitPlan plan_splits(int64_t nq, int64_t nk, int H, int requested, vggt_dtype d
     //   attention(s) = ceil(ktiles / s) * (full rounds + tail)
     //   merge(s)     = partial bytes / (bytes one slot-tile-time moves), s > 1
     const int64_t wg = ((nq + query_tile(dt) - 1) / query_tile(dt)) * H;
-    const int64_t slots = (int64_t)kAssumedCUs * kWorkgroupsPerCU;
+    const int64_t slots = (int64_t)kAssumedCUs * (dt == VGGT_F32 ? 2 : vggt::attn_bf16_workgroups_per_cu());
     double best = 1e300;
     for (int s = 1; s <= kMaxSplits && s <= ktiles; ++s) {
       const double rounds = (double)(wg * s) / (double)slots;

@@ -179,6 +179,7 @@ hipError_t launch_pool(const void* k, const void* v, void* kd, void* vd, bool bf
 // must be a multiple of the key tile).
 constexpr int kAttnKeyTile = 64;
 int attn_bf16_query_tile();
+int attn_bf16_workgroups_per_cu();
 int attn_f32_query_tile();
 
 }  // namespace vggt
