@@ -89,6 +89,8 @@ constexpr int NQB = VGGT_ATTN_NQB;  // 16-query MFMA column blocks per wave
 constexpr int QW = 16 * NQB;        // queries per wave
 constexpr int BQ = NW * QW;       // queries per workgroup
 constexpr int NSTAGE = VGGT_ATTN_NSTAGE;  // LDS ring depth (tiles in flight = NSTAGE - 1)
+static_assert(NQB >= 2 && NQB % 2 == 0, "scores and weights are double-buffered by step parity");
+static_assert(NSTAGE >= 2 && NSTAGE <= 4, "the tile waits cover at most two later tiles in flight");
 // exact pass: move m when a block's largest score exceeds it by kRaise; on the first tile
 // also when that score lies below kLow
 constexpr float kRaise = 32.0f;
