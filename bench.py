@@ -18,6 +18,7 @@ is timed on a row sample of the same step as the CPU baseline.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -223,6 +224,8 @@ def main() -> int:
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "arch": getattr(props, "gcnArchName", ""), "max_clock_mhz": _max_clock_mhz()},
         "input_gen_s": round(gen_s, 2),
+        # SHA-256 of the host bf16 bit patterns of the headline inputs, for reproduction
+        "input_sha256": {name: hashlib.sha256(a.tobytes()).hexdigest() for name, a in (("q", q), ("k", k), ("v", v))},
     }
 
     if not args.no_extras:
