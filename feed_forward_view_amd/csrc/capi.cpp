@@ -102,7 +102,10 @@ SplitPlan plan_splits(int64_t nq, int64_t nk, int H, int requested, vggt_dtype d
     //   attention(s) = ceil(ktiles / s) * (full rounds + tail)
     //   merge(s)     = partial bytes / (bytes one slot-tile-time moves), s > 1
     const int64_t wg = ((nq + query_tile(dt) - 1) / query_tile(dt)) * H;
-    const int64_t slots = (int64_t)kAssumedCUs * (dt == VGGT_F32 ? 2 : vggt::attn_bf16_workgroups_per_cu());
+    // resident workgroups per CU: the bf16 kernel's declared occupancy; the untuned fp32
+    // debug kernel is planned with the same two
+    const int per_cu = dt == VGGT_F32 ? 2 : vggt::attn_bf16_workgroups_per_cu();
+    const int64_t slots = (int64_t)kAssumedCUs * per_cu;
     double best = 1e300;
     for (int s = 1; s <= kMaxSplits && s <= ktiles; ++s) {
       const double rounds = (double)(wg * s) / (double)slots;
