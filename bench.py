@@ -39,7 +39,7 @@ PEAK_HBM_GBS = 8000.0
 # plain 1 GiB copy (profiles/attn_fwd_bf16_vggt-518-s32_counters.md).  Valid
 # only for the kernel source it was measured on.
 PROFILED_TRAFFIC = {
-    "kernel_source_sha256": "c492516f8cd8a978b3accfa30053b471d52b64d3294cac58dd110b42e5035b33",
+    "kernel_source_sha256": "c69df38f62d0c9b1ba38c352221403f174469dfa6a2e3328d99cf732ab432de8",
     "read_bytes": 1175.6e6,
     "write_bytes": 90.0e6,
 }

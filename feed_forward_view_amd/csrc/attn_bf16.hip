@@ -74,7 +74,12 @@ namespace {
 
 constexpr int D = kHeadDim;
 constexpr int BK = kAttnKeyTile;  // 64 keys per tile
-constexpr int NW = 4;             // waves per workgroup
+#ifndef VGGT_ATTN_NW
+#define VGGT_ATTN_NW 4
+#endif
+constexpr int NW = VGGT_ATTN_NW;  // waves per workgroup
+constexpr int CPW = 8 / NW;       // 1 KiB blocks of each tile that a wave copies
+constexpr int LPT = 2 * CPW;      // copies (K + V) per wave per tile
 #ifndef VGGT_ATTN_NSTAGE
 #define VGGT_ATTN_NSTAGE 4
 #endif
@@ -91,6 +96,7 @@ constexpr int BQ = NW * QW;       // queries per workgroup
 constexpr int NSTAGE = VGGT_ATTN_NSTAGE;  // LDS ring depth (tiles in flight = NSTAGE - 1)
 static_assert(NQB >= 2 && NQB % 2 == 0, "scores and weights are double-buffered by step parity");
 static_assert(NSTAGE >= 2 && NSTAGE <= 4, "the tile waits cover at most two later tiles in flight");
+static_assert(NW == 4 || NW == 8, "a tile is copied as 8 blocks of 1 KiB, split evenly over the waves");
 // exact pass: move m when a block's largest score exceeds it by kRaise; on the first tile
 // also when that score lies below kLow
 constexpr float kRaise = 32.0f;
@@ -115,6 +121,7 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else if constexpr (N == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
   else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
   else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
 }
@@ -192,17 +199,17 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
   const int q0 = qt * BQ + wave * QW;  // first query of this wave
   const bool active = q0 < nq_seq;
 
-  // ---- tile loads: each wave copies two 1 KiB blocks of the K tile and two of the V^T tile
+  // ---- tile loads: each wave copies CPW 1 KiB blocks of the K tile and CPW of the V^T tile
   const int ktile0 = kbeg / BK;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   auto issue = [&](int stage, int tile) {
     // wave-uniform base (scalar registers) + the lane's 16-byte unit
-    const u32x4* ks = ktg + (int64_t)(ktile0 + tile) * 512 + wave_u * 128;
-    const u32x4* vs = vtg + (int64_t)(ktile0 + tile) * 512 + wave_u * 128;
+    const u32x4* ks = ktg + (int64_t)(ktile0 + tile) * 512 + wave_u * (64 * CPW);
+    const u32x4* vs = vtg + (int64_t)(ktile0 + tile) * 512 + wave_u * (64 * CPW);
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      __builtin_amdgcn_global_load_lds((const void*)(ks + 64 * c + lane), (lds_void*)&sm.k[stage][(2 * wave_u + c) * 8][0], 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(vs + 64 * c + lane), (lds_void*)&sm.vt[stage][(2 * wave_u + c) * 8][0], 16, 0, 0);
+    for (int c = 0; c < CPW; ++c) {
+      __builtin_amdgcn_global_load_lds((const void*)(ks + 64 * c + lane), (lds_void*)&sm.k[stage][(CPW * wave_u + c) * 8][0], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(vs + 64 * c + lane), (lds_void*)&sm.vt[stage][(CPW * wave_u + c) * 8][0], 16, 0, 0);
     }
   };
 
@@ -415,9 +422,9 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
   auto land = [&](int tile) {
     const int ahead = min(NSTAGE - 2, ntiles - 1 - tile);  // tiles issued after `tile`
     if (ahead >= 2)
-      wait_vmcnt<8>();
+      wait_vmcnt<2 * LPT>();
     else if (ahead == 1)
-      wait_vmcnt<4>();
+      wait_vmcnt<LPT>();
     else
       wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
@@ -578,7 +585,7 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
 }  // namespace
 
 int attn_bf16_query_tile() { return BQ; }
-int attn_bf16_workgroups_per_cu() { return VGGT_ATTN_WPE; }
+int attn_bf16_workgroups_per_cu() { return VGGT_ATTN_WPE * 4 / NW; }  // waves per SIMD x 4 SIMDs
 
 hipError_t launch_attn_bf16(const AttnProblem& p, hipStream_t stream) {
   const int ntq = (p.nq + BQ - 1) / BQ;
