@@ -39,8 +39,8 @@ PEAK_HBM_GBS = 8000.0
 # plain 1 GiB copy (profiles/attn_fwd_bf16_vggt-518-s32_counters.md).  Valid
 # only for the kernel source it was measured on.
 PROFILED_TRAFFIC = {
-    "kernel_source_sha256": "c69df38f62d0c9b1ba38c352221403f174469dfa6a2e3328d99cf732ab432de8",
-    "read_bytes": 1175.6e6,
+    "kernel_source_sha256": "f91c40d75c56e26aefb57b8e3d5264f7987b39700b6eaf7048190049055efa82",
+    "read_bytes": 1177.2e6,
     "write_bytes": 90.0e6,
 }
 
@@ -53,11 +53,14 @@ def profiled_traffic():
     """Bytes per launch if the attention kernel is the one the counters were taken on, else None."""
     import hashlib
 
-    path = os.path.join(ROOT, "feed_forward_view_amd", "csrc", "attn_bf16.hip")
+    # the kernel's source and the header that fixes its LDS tile layout
+    h = hashlib.sha256()
     try:
-        sha = hashlib.sha256(open(path, "rb").read()).hexdigest()
+        for name in ("attn_bf16.hip", "common.h"):
+            h.update(open(os.path.join(ROOT, "feed_forward_view_amd", "csrc", name), "rb").read())
     except OSError:
         return None
+    sha = h.hexdigest()
     if sha != PROFILED_TRAFFIC["kernel_source_sha256"]:
         return None
     return PROFILED_TRAFFIC["read_bytes"] + PROFILED_TRAFFIC["write_bytes"]

@@ -12,21 +12,23 @@
 //
 // Two kernels, no atomics:
 //   attn_bwd_dq_kernel    one wave per 32 queries (two 16-query blocks), keys
-//                         streamed in 64-key tiles (K rows, V rows, K^T)
-//                         through LDS:
+//                         streamed in 64-key tiles (K rows, V rows) through
+//                         LDS:
 //                           S^T  = K Q^T - lse2      (accumulator input -lse2)
 //                           dP^T = V dO^T - D        (accumulator input -D)
 //                           dS^T = 2^(S^T) * dP^T
 //                           dQ^T += K^T dS^T
 //   attn_bwd_dkdv_kernel  one wave per 32 keys (two 16-key blocks), queries
-//                         streamed in 64-query tiles (Q rows, dO rows, Q^T,
-//                         dO^T, lse2, D):
+//                         streamed in 64-query tiles (Q rows, dO rows, lse2,
+//                         D):
 //                           S  = Q K^T - lse2,  dP = dO V^T - D
 //                           dV^T += dO^T P,      dK^T += Q^T dS
 // Both use v_mfma_f32_16x16x32_bf16 with the layout of the forward kernel:
 // the accumulator registers of two 16-row score blocks are, in order, the
-// bf16 B operand of the next product for their 32-row chunk, because the
-// transposed tiles store each chunk's rows in that operand order.  (Under
+// bf16 B operand of the next product for their 32-row chunk.  The A operands
+// of those products (K^T, dO^T, Q^T) are read from the row tiles in LDS with
+// transposing reads (ds_read_b64_tr_b16) that deliver each chunk's rows in
+// that operand order, so no transposed copy is made in memory.  (Under
 // sustained load this shape keeps a higher clock than 32x32x16 at the same
 // work.)  The query operand of the scores carries scale*log2(e) and is
 // rounded exactly as in the forward kernel, so the recomputed probabilities
@@ -51,11 +53,34 @@ typedef __attribute__((address_space(3))) void lds_void;
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  else if constexpr (N == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-  else if constexpr (N == 9) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+  else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  else if constexpr (N == 5) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 w) { return __builtin_bit_cast(bf16x8, w); }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// The A operand of a 16x16x32 product whose M dimension is the 64 channels of a row tile
+// (rows are keys or queries, 8 x 16-byte units per row, unit u at slot u ^ row_swz(row)):
+// channel block db (16 channels) of 32-row chunk c, the chunk's rows in operand order (lane l
+// holds channel 16db + l%16 of rows 4(l/16) + 0..3 and 16 + 4(l/16) + 0..3).  Two transposing
+// LDS reads: within each 16-lane group, lane 4r + q reads the 8 bytes of channels
+// 16db + 4q .. +3 of one row, and lane j of the group receives element j % 4 of lane
+// 4r' + j / 4's bytes as its element r', i.e. channel 16db + j of the four rows the group read.
+__device__ __forceinline__ bf16x8 read_tr_a(const u32x4 (&tile)[64][8], int c, int db, int lane) {
+  const int g = lane >> 4, r = (lane >> 2) & 3, q = lane & 3;
+  const int u = 2 * db + (q >> 1);
+  u32x2 half[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int row = 32 * c + 16 * h + 4 * g + r;
+    const char* src = (const char*)&tile[row][u ^ row_swz(row)] + 8 * (q & 1);
+    half[h] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)src));
+  }
+  return as_bf16x8(u32x4{half[0][0], half[0][1], half[1][0], half[1][1]});
+}
 
 // Workgroup barrier for the tile ring.  __syncthreads() would make the compiler drain every
 // outstanding copy first, including the next tile's, which was issued just before; the
@@ -91,9 +116,8 @@ __device__ __forceinline__ void store4(uint16_t* dst, const float* x, const f32x
 // ---------------------------------------------------------------------------
 
 struct SmemDq {
-  u32x4 k[2][64][8];   // K rows
+  u32x4 k[2][64][8];   // K rows (also read transposed: the A operand of dQ^T += K^T dS^T)
   u32x4 v[2][64][8];   // V rows
-  u32x4 kt[2][64][8];  // K^T
 };
 
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -111,7 +135,6 @@ void attn_bwd_dq_kernel(AttnBwdProblem p) {
   const int64_t tbase = ((int64_t)seq * p.H + head) * p.ntile * 512;
   const u32x4* kg = (const u32x4*)p.k_rows + tbase;
   const u32x4* vg = (const u32x4*)p.v_rows + tbase;
-  const u32x4* ktg = (const u32x4*)p.k_trans + tbase;
   const int64_t sbase = ((int64_t)seq * p.H + head) * p.ntile * 64;
 
   auto issue = [&](int stage, int tile) {
@@ -121,8 +144,6 @@ void attn_bwd_dq_kernel(AttnBwdProblem p) {
       const int row = (2 * wave + c) * 8;
       __builtin_amdgcn_global_load_lds((const void*)(kg + off + 64 * c), (lds_void*)&sm.k[stage][row][0], 16, 0, 0);
       __builtin_amdgcn_global_load_lds((const void*)(vg + off + 64 * c), (lds_void*)&sm.v[stage][row][0], 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(ktg + off + 64 * c), (lds_void*)&sm.kt[stage][row][0], 16, 0,
-                                       0);
     }
   };
   issue(0, 0);
@@ -176,7 +197,7 @@ void attn_bwd_dq_kernel(AttnBwdProblem p) {
     if (t + 1 < p.ntile) {
       tile_barrier();  // every wave is done with the stage tile t+1 goes to
       issue(stage ^ 1, t + 1);
-      wait_vmcnt<6>();  // tile t has landed (tile t+1 may still be in flight)
+      wait_vmcnt<4>();  // tile t has landed (tile t+1 may still be in flight)
     } else {
       wait_vmcnt<0>();
     }
@@ -195,10 +216,7 @@ void attn_bwd_dq_kernel(AttnBwdProblem p) {
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const int d = 16 * db + l16;
-        ktf[c][db] = as_bf16x8(sm.kt[stage][d][(4 * c + g) ^ col_swz(d)]);
-      }
+      for (int db = 0; db < 4; ++db) ktf[c][db] = read_tr_a(sm.k[stage], c, db, lane);
     const bool tail = t == p.ntile - 1 && 64 * p.ntile > p.n;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -254,10 +272,8 @@ void attn_bwd_dq_kernel(AttnBwdProblem p) {
 // ---------------------------------------------------------------------------
 
 struct SmemDkv {
-  u32x4 q[2][64][8];   // Q rows (scaled)
-  u32x4 d[2][64][8];   // dO rows
-  u32x4 qt[2][64][8];  // Q^T
-  u32x4 dt[2][64][8];  // dO^T
+  u32x4 q[2][64][8];   // Q rows, scaled (also read transposed: dK^T += Q^T dS)
+  u32x4 d[2][64][8];   // dO rows (also read transposed: dV^T += dO^T P)
   float st[2][2][64];  // lse2, D of the tile's 64 queries
 };
 
@@ -276,8 +292,6 @@ void attn_bwd_dkdv_kernel(AttnBwdProblem p) {
   const int64_t tbase = ((int64_t)seq * p.H + head) * p.ntile * 512;
   const u32x4* qg = (const u32x4*)p.q_rows + tbase;
   const u32x4* dg = (const u32x4*)p.do_rows + tbase;
-  const u32x4* qtg = (const u32x4*)p.q_trans + tbase;
-  const u32x4* dtg = (const u32x4*)p.do_trans + tbase;
   const int64_t sbase = ((int64_t)seq * p.H + head) * p.ntile * 64;
 
   auto issue = [&](int stage, int tile) {
@@ -287,10 +301,6 @@ void attn_bwd_dkdv_kernel(AttnBwdProblem p) {
       const int row = (2 * wave + c) * 8;
       __builtin_amdgcn_global_load_lds((const void*)(qg + off + 64 * c), (lds_void*)&sm.q[stage][row][0], 16, 0, 0);
       __builtin_amdgcn_global_load_lds((const void*)(dg + off + 64 * c), (lds_void*)&sm.d[stage][row][0], 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(qtg + off + 64 * c), (lds_void*)&sm.qt[stage][row][0], 16, 0,
-                                       0);
-      __builtin_amdgcn_global_load_lds((const void*)(dtg + off + 64 * c), (lds_void*)&sm.dt[stage][row][0], 16, 0,
-                                       0);
     }
     // 512 bytes of statistics: waves 0-1 bring lse2, waves 2-3 bring D (8 lanes x 16 bytes each)
     if (lane < 8) {
@@ -332,7 +342,7 @@ void attn_bwd_dkdv_kernel(AttnBwdProblem p) {
     if (t + 1 < p.ntile) {
       tile_barrier();  // every wave is done with the stage tile t+1 goes to
       issue(stage ^ 1, t + 1);
-      wait_vmcnt<9>();  // tile t has landed (tile t+1 may still be in flight)
+      wait_vmcnt<5>();  // tile t has landed (tile t+1 may still be in flight)
     } else {
       wait_vmcnt<0>();
     }
@@ -367,10 +377,8 @@ void attn_bwd_dkdv_kernel(AttnBwdProblem p) {
       bf16x8 dtf[4], qtf[4];
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const int d = 16 * db + l16;
-        const int slot = (4 * c + g) ^ col_swz(d);
-        dtf[db] = as_bf16x8(sm.dt[stage][d][slot]);
-        qtf[db] = as_bf16x8(sm.qt[stage][d][slot]);
+        dtf[db] = read_tr_a(sm.d[stage], c, db, lane);
+        qtf[db] = read_tr_a(sm.q[stage], c, db, lane);
       }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -403,7 +411,7 @@ void attn_bwd_dkdv_kernel(AttnBwdProblem p) {
       const int d0 = 16 * db + 4 * g;
       const float xk[4] = {dka[kb][db][0], dka[kb][db][1], dka[kb][db][2], dka[kb][db][3]};
       const float xv[4] = {dva[kb][db][0], dva[kb][db][1], dva[kb][db][2], dva[kb][db][3]};
-      store4(dkp, xk, trow, d0, p.scale);
+      store4(dkp, xk, trow, d0, p.scale / p.scale_log2);  // the Q rows carry scale * log2(e)
       store4(dvp, xv, nullptr, d0, 1.0f);
     }
   }

@@ -1092,11 +1092,11 @@ VGGT_API vggt_status vggt_global_attn_train(const void* q, const void* k, const 
 
 namespace {
 
-// Workspace of one backward call.  bf16: RoPE table, rotated copies of Q and K,
-// seven tile sets (K rows, V rows, K^T, scaled Q rows, dO rows, Q^T, dO^T) and
-// the per-row statistics; fp32: rotated copies and rotated-frame gradients.
+// Workspace of one backward call.  bf16: RoPE table, a rotated copy of K, four
+// row-tile sets (K, V, scaled Q, dO) and the per-row statistics; fp32: rotated
+// copies and rotated-frame gradients.
 struct BwdLayout {
-  size_t table = 0, qr = 0, kr = 0, tiles[7] = {0, 0, 0, 0, 0, 0, 0}, lse2 = 0, dsum = 0, dqr = 0, dkr = 0;
+  size_t table = 0, qr = 0, kr = 0, tiles[4] = {0, 0, 0, 0}, lse2 = 0, dsum = 0, dqr = 0, dkr = 0;
   size_t total = 0;
   int nseq = 1, n = 0, ntile = 0;
 };
@@ -1113,9 +1113,9 @@ BwdLayout plan_bwd(bool global, int S, int T, int H, bool rope, vggt_dtype dt) {
   L.ntile = (L.n + 63) / 64;
   const size_t tensor = (size_t)S * T * H * vggt::kHeadDim * elem_size(dt);
   if (dt == VGGT_BF16) {
+    // the kernels read the transposes they need from these tiles in LDS
     if (rope) {
       add_b(L, L.table, (size_t)T * 32 * 8);
-      add_b(L, L.qr, tensor);
       add_b(L, L.kr, tensor);
     }
     const size_t tiles = (size_t)L.nseq * H * L.ntile * 64 * vggt::kHeadDim * 2;
@@ -1186,24 +1186,18 @@ vggt_status attn_backward(bool global, const void* q, const void* k, const void*
   if (e != hipSuccess) return device_error("backward pre-pass", e);
   if (dt == VGGT_BF16) {
     const void* table = nullptr;
-    const void* qr = q;
     const void* kr = k;
     if (pos) {
       e = vggt::launch_rope_table(pos, T, (double)base, ws + L.table, st);
-      if (e == hipSuccess) e = vggt::launch_rope(q, ws + L.qr, true, N, T, H, pos, (double)base, st);
       if (e == hipSuccess) e = vggt::launch_rope(k, ws + L.kr, true, N, T, H, pos, (double)base, st);
       if (e != hipSuccess) return device_error("backward rotation", e);
       table = ws + L.table;
-      qr = ws + L.qr;
       kr = ws + L.kr;
     }
     char* tk = ws + L.tiles[0];
     char* tv = ws + L.tiles[1];
-    char* tkt = ws + L.tiles[2];
-    char* tq = ws + L.tiles[3];
-    char* tdo = ws + L.tiles[4];
-    char* tqt = ws + L.tiles[5];
-    char* tdot = ws + L.tiles[6];
+    char* tq = ws + L.tiles[2];
+    char* tdo = ws + L.tiles[3];
     const int n = L.n, ns = L.nseq;
     e = vggt::launch_k_tiles_bf16(vggt::contiguous_keys(k, n), tk, ns, n, H, table, T, nullptr,
                                   nullptr, 0.0f, st);
@@ -1211,17 +1205,11 @@ vggt_status attn_backward(bool global, const void* q, const void* k, const void*
       e = vggt::launch_k_tiles_bf16(vggt::contiguous_keys(v, n), tv, ns, n, H, nullptr, 1, nullptr,
                                     nullptr, 0.0f, st);
     if (e == hipSuccess)
-      e = vggt::launch_v_tiles_bf16(vggt::contiguous_keys(kr, n), tkt, ns, n, H, st);
-    if (e == hipSuccess)
       e = vggt::launch_k_tiles_bf16(vggt::contiguous_keys(q, n), tq, ns, n, H, table, T, nullptr, nullptr, 0.0f, st,
                                     c);
     if (e == hipSuccess)
       e = vggt::launch_k_tiles_bf16(vggt::contiguous_keys(dout, n), tdo, ns, n, H, nullptr, 1, nullptr, nullptr, 0.0f,
                                     st);
-    if (e == hipSuccess)
-      e = vggt::launch_v_tiles_bf16(vggt::contiguous_keys(qr, n), tqt, ns, n, H, st);
-    if (e == hipSuccess)
-      e = vggt::launch_v_tiles_bf16(vggt::contiguous_keys(dout, n), tdot, ns, n, H, st);
     if (e != hipSuccess) return device_error("backward tile pre-pass", e);
     vggt::AttnBwdProblem p;
     std::memset(&p, 0, sizeof(p));
@@ -1233,11 +1221,8 @@ vggt_status attn_backward(bool global, const void* q, const void* k, const void*
     p.rope_T = T;
     p.k_rows = tk;
     p.v_rows = tv;
-    p.k_trans = tkt;
     p.q_rows = tq;
     p.do_rows = tdo;
-    p.q_trans = tqt;
-    p.do_trans = tdot;
     p.lse2 = lse2;
     p.dsum = dsum;
     p.dq = dq;

@@ -30,13 +30,20 @@ __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w 
 // 16-byte slot swizzles of the 8 KiB tile images (64 rows of 8 x 16-byte units) that the
 // attention kernels copy linearly into LDS: unit u of row r sits at slot u ^ row_swz(r) in
 // row tiles (rows are keys or queries) and at slot u ^ col_swz(d) in transposed tiles (rows
-// are channels).  An MFMA operand read (ds_read_b128) has lane l read one unit of row
-// base + l % 32; the swizzle spreads each group of rows read together over distinct banks.
-#ifndef VGGT_TILE_SWZ
-#define VGGT_TILE_SWZ 2
-#endif
-__device__ __forceinline__ int row_swz(int r) { return VGGT_TILE_SWZ == 1 ? (r & 7) : ((r >> 1) & 7); }
-__device__ __forceinline__ int col_swz(int d) { return VGGT_TILE_SWZ == 1 ? ((d ^ (d >> 3)) & 7) : ((d >> 1) & 7); }
+// are channels).  The LDS of gfx950 has 64 four-byte banks (two 128-byte rows of the tile per
+// bank line).  It serves a ds_read_b128 in four passes of 16 lanes, each pass four 4-lane
+// blocks (lanes 4b..4b+3) whose block numbers b share bit 3 and the parity of bits 0-2, and a
+// ds_read_b64_tr_b16 in two passes of 32 lanes (the two half-waves); both lane groupings
+// were measured with a bank-conflict counter.  The operand reads are
+//   * ds_read_b128: lane l reads unit 4c + l/16 of row base + l % 16;
+//   * ds_read_b64_tr_b16 (gradient kernels): the lanes of a half-wave read 32 bytes (units
+//     2db, 2db + 1) of each of 8 consecutive rows.
+// row_swz = r & 6 makes both conflict-free: in a b128 pass the four blocks cover rows
+// {4i..4i+3} of two units of opposite parity, and (r & 1, u ^ (r & 6)) differs for all 16
+// lanes; in a transposing half-wave, (r & 1, (r >> 1) & 3) differs for all 8 rows.  col_swz
+// serves only b128 reads.
+__device__ __forceinline__ int row_swz(int r) { return r & 6; }
+__device__ __forceinline__ int col_swz(int d) { return (d >> 1) & 7; }
 
 // Workgroups are dealt round-robin to the 8 XCDs; this maps the hardware id w
 // of nwg workgroups to a logical id such that each XCD receives a contiguous
@@ -98,11 +105,8 @@ struct AttnBwdProblem {
   int rope_T;
   const void* k_rows;      // K rotated, row tiles (the forward's K tiles)
   const void* v_rows;      // V, row tiles
-  const void* k_trans;     // K rotated, transposed tiles
   const void* q_rows;      // Q rotated and scaled by scale*log2(e), row tiles
   const void* do_rows;     // dO, row tiles
-  const void* q_trans;     // Q rotated, transposed tiles
-  const void* do_trans;    // dO, transposed tiles
   const float* lse2;       // [nseq][H][ntile*64]: minus the log2-normaliser of each query row (-inf past the end)
   const float* dsum;       // [nseq][H][ntile*64]: minus rowsum(dO * O) (0 past the end)
   void* dq;                // [tokens][H][64] bf16 outputs

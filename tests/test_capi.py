@@ -234,11 +234,12 @@ def test_backward_arguments(L):
     BF16, F32 = 0, 1
     S, T, H = 4, 100, 2
     n, tiles = S * T, (S * T + 63) // 64
-    # bf16 global: seven tile sets plus two statistics rows per head; RoPE adds the table and rotated copies
+    # bf16 global: four row-tile sets (K, V, Q, dO) plus two statistics rows per head; RoPE adds the
+    # table and a rotated copy of K
     base = L.vggt_attn_backward_workspace(S, T, H, 1, 0, BF16)
-    assert base >= 7 * H * tiles * 64 * 64 * 2 + 2 * H * tiles * 64 * 4
-    assert L.vggt_attn_backward_workspace(S, T, H, 1, 1, BF16) >= base + 2 * n * H * 64 * 2
-    assert L.vggt_attn_backward_workspace(S, T, H, 0, 0, BF16) >= 7 * S * H * 2 * 64 * 64 * 2
+    assert base >= 4 * H * tiles * 64 * 64 * 2 + 2 * H * tiles * 64 * 4
+    assert L.vggt_attn_backward_workspace(S, T, H, 1, 1, BF16) >= base + n * H * 64 * 2 + T * 32 * 8
+    assert L.vggt_attn_backward_workspace(S, T, H, 0, 0, BF16) >= 4 * S * H * 2 * 64 * 64 * 2
     assert L.vggt_attn_backward_workspace(S, T, H, 1, 1, F32) >= 4 * n * H * 64 * 4
     assert L.vggt_attn_backward_workspace(S, 0, H, 1, 0, BF16) == 0
     b = L.vggt_global_attn_backward
