@@ -93,9 +93,9 @@ struct AttnProblem {
 
 // Attention gradients (bf16).  Sequences, strides and counts as in
 // AttnProblem with nq == nk and q/k sequences T tokens apart (frame) or one
-// sequence (global).  Tile buffers: [nseq][H][ntile][64 x 64] in the forward
-// kernel's layouts -- "row" tiles as its K tiles, "transposed" tiles as its
-// V^T tiles.
+// sequence (global).  Tile buffers: [nseq][H][ntile][64 x 64] row tiles in
+// the layout of the forward kernel's K tiles; the kernels read the transposed
+// operands they need from these tiles in LDS.
 struct AttnBwdProblem {
   const void* q;           // [tokens][H][64] bf16: Q fragments of the dQ kernel
   const void* dout;        // [tokens][H][64] bf16: dO fragments of the dQ kernel
