@@ -135,18 +135,25 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-// Interleave hints for the scheduler, one per half step: 8 x (1 MFMA, 1 exponential, 1 other
-// VALU op), optionally with one LDS fragment read per MFMA.
+// Interleave hints for the scheduler: the first half of a step takes 8 x (1 MFMA, 1
+// exponential, 1 other VALU op); the second half is two quarters of 4 x (...), the first of
+// which also takes the step's LDS fragment reads (two per MFMA) when it has any.
 #define VGGT_INTERLEAVE8()                                     \
   _Pragma("unroll") for (int _i = 0; _i < 8; ++_i) {           \
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         \
     __builtin_amdgcn_sched_group_barrier(0x400, 1, 0);         \
     __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);         \
   }
-#define VGGT_INTERLEAVE8_DS()                                  \
-  _Pragma("unroll") for (int _i = 0; _i < 8; ++_i) {           \
+#define VGGT_INTERLEAVE4()                                     \
+  _Pragma("unroll") for (int _i = 0; _i < 4; ++_i) {           \
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         \
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);         \
+    __builtin_amdgcn_sched_group_barrier(0x400, 1, 0);         \
+    __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);         \
+  }
+#define VGGT_INTERLEAVE4_DS2()                                 \
+  _Pragma("unroll") for (int _i = 0; _i < 4; ++_i) {           \
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         \
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);         \
     __builtin_amdgcn_sched_group_barrier(0x400, 1, 0);         \
     __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);         \
   }
@@ -342,20 +349,27 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
       for (int kb = 0; kb < 4; ++kb)
         sd[kb] = mfma(kf[kb][dc], qf[qb][dc], dc == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : sd[kb]);
   };
-  // O^T += V^T P^T and the row sums += 1 P^T of query block qb
+  // channel half dc of S^T of query block qb (four independent products)
+  auto qk_dc = [&](f32x4 (&sd)[4], int qb, int dc) {
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+      sd[kb] = mfma(kf[kb][dc], qf[qb][dc], dc == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : sd[kb]);
+  };
+  // O^T += V^T P^T and the row sums += 1 P^T of query block qb; the two row-sum products,
+  // which accumulate into one register, are issued eight MFMAs apart
   auto pv = [&](const u32x4 (&pf)[2], int qb) {
+    lrow[qb] = mfma(ones, __builtin_bit_cast(bf16x8, pf[0]), lrow[qb]);
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int db = 0; db < 4; ++db) o[qb][db] = mfma(vf[c][db], __builtin_bit_cast(bf16x8, pf[c]), o[qb][db]);
-#pragma unroll
-    for (int c = 0; c < 2; ++c) lrow[qb] = mfma(ones, __builtin_bit_cast(bf16x8, pf[c]), lrow[qb]);
+    lrow[qb] = mfma(ones, __builtin_bit_cast(bf16x8, pf[1]), lrow[qb]);
   };
-  // P = 2^(S - m) of 32-key chunk c of one query block as the bf16 B operand of P V
-  // (GEN: m of the lane's query is subtracted; else m = 0)
-  auto soft_c = [&](const f32x4 (&sc)[4], int c, auto gen_c, float m, u32x4& pf) {
+  // P = 2^(S - m) of 32-key chunk c of one query block as the bf16 B operand of P V, its
+  // register pairs e0 .. e1-1 (GEN: m of the lane's query is subtracted; else m = 0)
+  auto soft_e = [&](const f32x4 (&sc)[4], int c, auto gen_c, float m, u32x4& pf, int e0, int e1) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
+    for (int e = e0; e < e1; ++e) {
       const f32x4& sb = sc[2 * c + (e >> 1)];
       float a = sb[2 * (e & 1)], b = sb[2 * (e & 1) + 1];
       if constexpr (decltype(gen_c)::value) {
@@ -364,6 +378,9 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
       }
       pf[e] = pack_bf16x2(__builtin_amdgcn_exp2f(a), __builtin_amdgcn_exp2f(b));
     }
+  };
+  auto soft_c = [&](const f32x4 (&sc)[4], int c, auto gen_c, float m, u32x4& pf) {
+    soft_e(sc, c, gen_c, m, pf, 0, 4);
   };
   // largest of the lane's 16 scores of one query block
   auto smax = [&](const f32x4 (&sc)[4]) -> float {
@@ -475,20 +492,25 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
     __builtin_amdgcn_sched_barrier(0);
     // second half: S^T of the next step's block
     if constexpr (b == 0) read_v(stage);
-    if constexpr (b < NQB - 1) {
-      qk(s[nxt], b + 1);
-    } else if (!last) {
-      qk(s[nxt], 0);
-    }
+    constexpr int nb = b < NQB - 1 ? b + 1 : 0;
+    const bool has_next = b < NQB - 1 || !last;
     if constexpr (exact && first) {
+      if (has_next) qk(s[nxt], nb);
       slow(s[cur], b, true, pp[cur]);
     } else {
-      soft_c(s[cur], 1, exact_c, mrow[b], pp[cur][1]);
+      // split again, so that each key block's second channel half is issued four MFMAs
+      // after its first (left to itself the scheduler pairs some of them back to back)
+      if (has_next) qk_dc(s[nxt], nb, 0);
+      soft_e(s[cur], 1, exact_c, mrow[b], pp[cur][1], 0, 2);
       if constexpr (b == 0) {
-        VGGT_INTERLEAVE8_DS();
+        VGGT_INTERLEAVE4_DS2();
       } else {
-        VGGT_INTERLEAVE8();
+        VGGT_INTERLEAVE4();
       }
+      __builtin_amdgcn_sched_barrier(0);
+      if (has_next) qk_dc(s[nxt], nb, 1);
+      soft_e(s[cur], 1, exact_c, mrow[b], pp[cur][1], 2, 4);
+      VGGT_INTERLEAVE4();
       if constexpr (exact) {
         if (__any(smax(s[cur]) - mrow[b] > kRaise)) slow(s[cur], b, false, pp[cur]);
       }
