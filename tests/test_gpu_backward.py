@@ -80,6 +80,42 @@ def test_backward_small_full(dtype, rope, glob):
     check_grad(to_f64(dv), rv, f"{tag} dv", bf16)
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("glob", [True, False])
+@pytest.mark.parametrize("shape", ["one_tile", "whole_tiles"])
+def test_backward_tile_edges(dtype, glob, shape):
+    """Key and query ranges at tile edges: one frame of 7 x 7 patches + 5 special tokens
+    (54 rows: a single ragged tile, the first tile also the last), and frames of 8 x 8
+    patches with no special tokens (64 rows: whole tiles, nothing masked)."""
+    if shape == "one_tile":
+        wl = workload.Workload("t", 81, S=1, gh=7, gw=7, n_special=5, patch_begin=5, H=2)
+    else:
+        wl = workload.Workload("t", 82, S=2, gh=8, gw=8, n_special=0, patch_begin=0, H=2)
+    S, T, H = wl.S, wl.T, wl.H
+    q, k, v = wl.qkv_bf16() if dtype == torch.bfloat16 else wl.qkv_f32()
+    g = _dout(0xD0D1, (S, T, H, 64), dtype)
+    pos = wl.positions()
+    qd, kd, vd, gd = to_dev(q), to_dev(k), to_dev(v), to_dev(g)
+    pd = torch.from_numpy(pos).to(dev())
+    bf16 = dtype == torch.bfloat16
+    tag = f"{shape} {'global' if glob else 'frame'} {'bf16' if bf16 else 'f32'}"
+    if glob:
+        o, lse = ffv.vggt_global_attn_train(qd, kd, vd, pos_yx=pd)
+        dq, dk, dv = ffv.vggt_global_attn_backward(qd, kd, vd, o, gd, lse, pos_yx=pd)
+        rq, rk, rv, rl = oracle.global_attn_backward(q, k, v, g, S, T, pos=pos)
+    else:
+        o, lse = ffv.vggt_frame_attn_train(qd, kd, vd, pos_yx=pd)
+        dq, dk, dv = ffv.vggt_frame_attn_backward(qd, kd, vd, o, gd, lse, pos_yx=pd)
+        rq, rk, rv, rl = oracle.frame_attn_backward(q, k, v, g, S, T, pos=pos)
+    torch.cuda.synchronize()
+    lmax = float(np.abs(lse.cpu().numpy().astype(np.float64) - rl).max())
+    print(f"{tag} lse: max_abs {lmax:.3e}")
+    assert lmax <= (1e-2 if bf16 else 1e-5)
+    check_grad(to_f64(dq), rq, f"{tag} dq", bf16)
+    check_grad(to_f64(dk), rk, f"{tag} dk", bf16)
+    check_grad(to_f64(dv), rv, f"{tag} dv", bf16)
+
+
 def test_backward_is_deterministic_and_matches_plain_forward():
     wl = workload.Workload("t", 62, S=2, gh=12, gw=12, n_special=5, patch_begin=5, H=3)
     q, k, v = wl.qkv_bf16()
