@@ -42,9 +42,10 @@
 //
 // Softmax reference, optimistic.  The first pass keeps m = 0 for every row
 // and checks nothing per tile.  At the end a row is accepted when its sum l
-// lies in [2^-64, 2^100]: then no weight overflowed and the largest is at
-// least 2^-64 / N, far inside the normal range of bf16 and fp32, so the pass
-// computed the same softmax as any other reference up to rounding.  If any row
+// lies in [2^-64, 2^100] and its un-normalised output is finite: then no
+// weight or product overflowed and the largest weight is at least 2^-64 / N,
+// far inside the normal range of bf16 and fp32, so the pass computed the same
+// softmax as any other reference up to rounding.  If any row
 // of the workgroup fails (logits in the hundreds, or rows whose scores all lie
 // far below zero), the workgroup reruns its key range exactly: the first tile
 // sets a per-row m, every block's largest score is checked against it, and a
@@ -94,7 +95,10 @@ constexpr int NQB = VGGT_ATTN_NQB;  // 16-query MFMA column blocks per wave
 constexpr int QW = 16 * NQB;        // queries per wave
 constexpr int BQ = NW * QW;       // queries per workgroup
 constexpr int NSTAGE = VGGT_ATTN_NSTAGE;  // LDS ring depth (tiles in flight = NSTAGE - 1)
-static_assert(NQB >= 2 && NQB % 2 == 0, "scores and weights are double-buffered by step parity");
+// NQB >= 4: a tile's V fragments are read in step 0 and its ring slot is refilled after the
+// barrier of step NQB - 2; with NQB = 2 these would be the same step, and a faster wave's
+// refill could overwrite the slot while a slower wave's fragment reads are in flight
+static_assert(NQB >= 4 && NQB % 2 == 0, "scores and weights are double-buffered by step parity");
 static_assert(NSTAGE >= 2 && NSTAGE <= 4, "the tile waits cover at most two later tiles in flight");
 static_assert(NW == 4 || NW == 8, "a tile is copied as 8 blocks of 1 KiB, split evenly over the waves");
 // exact pass: move m when a block's largest score exceeds it by kRaise; on the first tile
@@ -515,6 +519,10 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
         if (__any(smax(s[cur]) - mrow[b] > kRaise)) slow(s[cur], b, false, pp[cur]);
       }
     }
+    // the step's weights are complete here: without this use the compiler sinks their
+    // exponentials past the tile wait and barrier below, next to their first use in the
+    // following step, which then starts with a run of VALU work and no MFMA beside it
+    asm volatile("" ::"v"(pp[cur][0]), "v"(pp[cur][1]));
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (b == NQB - 2) {
       if (!last) {
@@ -551,11 +559,20 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
   // reruns the key range with the exact per-row reference.
   if (active) {
     pass(no{});
+    // and its un-normalised output must be finite: weights up to 2^100 times values
+    // beyond about 2^28 overflow the float32 accumulators even when l is in range
     bool bad = false;
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
       const float l = lrow[qb][0];
-      if (q0 + 16 * qb + l16 < nq_seq && !(l >= 0x1p-64f && l <= 0x1p100f)) bad = true;
+      float omax = 0.0f;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) omax = fmaxf(omax, __builtin_fabsf(o[qb][db][r]));
+      // a NaN fails both comparisons
+      const bool ok = l >= 0x1p-64f && l <= 0x1p100f && omax <= 0x1p127f;
+      if (q0 + 16 * qb + l16 < nq_seq && !ok) bad = true;
     }
     if (__any(bad) && lane == 0) sm.redo = 1;
   } else {
