@@ -1,12 +1,13 @@
 """GPU parity: the HIP library (through the C ABI) against the float64 oracle.
 
-bf16 bar: max |gpu - oracle| <= 2e-2 and mean |gpu - oracle| <= 2e-3 per
-output tensor, for unit-normal Q/K/V.  fp32 debug bar: NRMSE <= 1e-5
-(sqrt(mean(err^2)) / sqrt(mean(ref^2))).  Small shapes are compared in full;
-the full-size workloads are compared on sampled query rows (every special
-token of the first and last frame, the first and last rows, the rows around
-query-tile boundaries, the last partial tile and seeded random rows) in the
-launch configuration the benchmark times.
+Bars (tests/checks.py): bf16 max |gpu - oracle| <= 2e-2, mean <= 2e-3, NRMSE
+<= 1e-2 and max <= 0.25 rms(oracle) per output tensor, for unit-normal Q/K/V;
+fp32 debug NRMSE <= 1e-5 (sqrt(mean(err^2)) / sqrt(mean(ref^2))).  Small
+shapes and the S = 8 VGGT-1B workload (N = 10992) are compared on every row;
+the larger workloads on sampled query rows (every special token of the first
+and last frame, the first and last rows, the rows around query-tile
+boundaries, the last partial tile and seeded random rows) in the launch
+configuration the benchmark times.
 """
 import functools
 
@@ -17,10 +18,10 @@ import torch
 import feed_forward_view_amd as ffv
 import oracle
 import workload
+from checks import check_bf16, check_f32, check_same_up_to_sum_order  # noqa: F401
 
 pytestmark = pytest.mark.gpu
 
-BF16_MAX, BF16_MEAN, F32_NRMSE = 2e-2, 2e-3, 1e-5
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -47,21 +48,6 @@ def to_f64(t: torch.Tensor) -> np.ndarray:
     if t.dtype == torch.bfloat16:
         return oracle.to_f64(t.view(torch.int16).cpu().numpy().view(np.uint16))
     return t.cpu().numpy().astype(np.float64)
-
-
-def check_bf16(got: np.ndarray, ref: np.ndarray, label: str):
-    err = np.abs(got.reshape(ref.shape) - ref)
-    mx, mean = float(err.max()), float(err.mean())
-    print(f"{label}: max_abs {mx:.3e} mean_abs {mean:.3e} (ref max {np.abs(ref).max():.3f})")
-    assert np.isfinite(got).all(), label
-    assert mx <= BF16_MAX and mean <= BF16_MEAN, f"{label}: max {mx:.3e} mean {mean:.3e}"
-
-
-def check_f32(got: np.ndarray, ref: np.ndarray, label: str):
-    diff = got.reshape(ref.shape) - ref
-    nrmse = float(np.sqrt(np.mean(diff ** 2)) / max(np.sqrt(np.mean(ref ** 2)), 1e-30))
-    print(f"{label}: nrmse {nrmse:.3e} max_abs {np.abs(diff).max():.3e}")
-    assert nrmse <= F32_NRMSE, f"{label}: nrmse {nrmse:.3e}"
 
 
 def sample_rows(n: int, T: int, S: int, seed: int, n_random: int = 96, tile: int = 256) -> np.ndarray:
@@ -192,6 +178,27 @@ def test_deterministic_repeat():
     assert torch.equal(c.view(torch.int16), d.view(torch.int16))
 
 
+def test_side_stream_launch():
+    """Calls on a stream other than torch's current one: the workspace and the
+    outputs come from that stream's pool, so the current stream's allocations
+    made while the kernels run cannot take their memory."""
+    wl, q, k, v = inputs("vggt-224-s4")
+    pos = wl.positions()
+    qd, kd, vd, pd = to_dev(q), to_dev(k), to_dev(v), torch.from_numpy(pos).to(dev())
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    fo = ffv.vggt_frame_attn(qd, kd, vd, pos_yx=pd, stream=side)
+    go = ffv.vggt_global_attn(qd, kd, vd, pos_yx=pd, kv_splits=2, stream=side)
+    xo = ffv.vggt_global_attn(qd, kd, vd, pos_yx=pd, kv_splits=3, stream=side)
+    churn = [torch.full((1 << 20,), float(i), device=dev()) for i in range(16)]
+    side.synchronize()
+    del churn
+    check_bf16(to_f64(fo), oracle.frame_attn(q, k, v, wl.S, wl.T, pos=pos), "side stream frame")
+    ref = oracle.global_attn(q, k, v, wl.S, wl.T, pos=pos)
+    check_bf16(to_f64(go), ref, "side stream global splits=2")
+    check_bf16(to_f64(xo), ref, "side stream global splits=3")
+
+
 def test_frame_permutation_equivariance_gpu():
     wl, q, k, v = inputs("vggt-224-s4")
     pos = torch.from_numpy(wl.positions()).to(dev())
@@ -200,8 +207,8 @@ def test_frame_permutation_equivariance_gpu():
     g = ffv.vggt_global_attn(qd, kd, vd, pos_yx=pos, kv_splits=1)
     gp = ffv.vggt_global_attn(qd[perm].contiguous(), kd[perm].contiguous(), vd[perm].contiguous(), pos_yx=pos,
                               kv_splits=1)
-    err = (gp.float() - g[perm].float()).abs().max().item()
-    assert err <= 2 * 2.0 ** -8, err  # equal up to the summation order of the keys
+    # equal up to the summation order of the keys
+    check_same_up_to_sum_order(to_f64(gp), to_f64(g[perm].contiguous()), "frame permutation")
 
 
 # ---------------------------------------------------------------------------
@@ -281,7 +288,25 @@ def test_xattn_small_full_and_unit_window():
 # Full-size workloads on sampled rows
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name", ["vggt-518-s8", "vggt-518-s32", "omega-512-s64"])
+def test_s8_frame_all_rows():
+    """VGGT-1B at 8 frames: frame attention compared on every row."""
+    wl, q, k, v = inputs("vggt-518-s8")
+    pos = wl.positions()
+    qd, kd, vd, pd = to_dev(q), to_dev(k), to_dev(v), torch.from_numpy(pos).to(dev())
+    fo = ffv.vggt_frame_attn(qd, kd, vd, pos_yx=pd, rope_base=100.0)
+    check_bf16(to_f64(fo), oracle.frame_attn(q, k, v, wl.S, wl.T, pos=pos), "vggt-518-s8 frame (all rows)")
+
+
+def test_s8_global_all_rows():
+    """VGGT-1B at 8 frames: global attention (N = 10992) compared on every row."""
+    wl, q, k, v = inputs("vggt-518-s8")
+    pos = wl.positions()
+    qd, kd, vd, pd = to_dev(q), to_dev(k), to_dev(v), torch.from_numpy(pos).to(dev())
+    go = ffv.vggt_global_attn(qd, kd, vd, pos_yx=pd, rope_base=100.0)
+    check_bf16(to_f64(go), oracle.global_attn(q, k, v, wl.S, wl.T, pos=pos), "vggt-518-s8 global (all rows)")
+
+
+@pytest.mark.parametrize("name", ["vggt-518-s32", "omega-512-s64"])
 def test_full_size_frame_and_global(name):
     wl, q, k, v = inputs(name)
     pos = wl.positions()
@@ -324,11 +349,11 @@ def test_split_count_independence_full_size():
     outs = []
     for splits in (1, 2, 3, 7):
         go = ffv.vggt_global_attn(qd, kd, vd, pos_yx=pd, kv_splits=splits)
-        outs.append(go.float())
-        check_bf16(to_f64(go).reshape(wl.N, wl.H, 64)[rows], ref, f"s8 global splits={splits}")
-    for o in outs[1:]:
+        outs.append(to_f64(go))
+        check_bf16(outs[-1].reshape(wl.N, wl.H, 64)[rows], ref, f"s8 global splits={splits}")
+    for splits, o in zip((2, 3, 7), outs[1:]):
         # different split counts only reorder fp32 sums: results agree to bf16 rounding
-        assert (o - outs[0]).abs().max().item() <= 2.0 ** -7
+        check_same_up_to_sum_order(o, outs[0], f"s8 global splits={splits} vs 1")
 
 
 def test_empty_batch_through_the_binding():

@@ -8,7 +8,8 @@ import torch
 import feed_forward_view_amd as ffv
 import oracle
 import workload
-from test_gpu_parity import check_bf16, check_f32, dev, sample_rows, to_dev, to_f64
+from checks import check_bf16, check_f32
+from test_gpu_parity import dev, sample_rows, to_dev, to_f64
 
 pytestmark = pytest.mark.gpu
 

@@ -42,7 +42,8 @@ import torch
 import feed_forward_view_amd as ffv
 import oracle
 import workload
-from test_gpu_parity import check_bf16, dev, to_dev, to_f64
+from checks import check_bf16
+from test_gpu_parity import dev, to_dev, to_f64
 from test_gpu_backward import check_grad
 
 pytestmark = pytest.mark.gpu
@@ -211,3 +212,48 @@ def test_single_tile_key_range(kind, dtype):
         check_bf16(to_f64(go), ref, f"global one tile {tag}")
     else:
         _check_f32(to_f64(go), ref, f"global one tile {tag}", _score_bound(q1, k1, 1, T, True, scale))
+
+
+VSHIFT = 34  # V scaled by 2^34
+
+
+def _large_value_case(dtype):
+    """3 frames of 86 tokens, 2 heads: channel 63 is 256 on every query and
+    2.8125 on every key, so at scale ln2/8 each score sits near 90 log2 units
+    and every row's sum of weights 2^s lies in [2^96.5, 2^98.7], inside the
+    optimistic pass's bound on the row sum.  V is scaled by 2^34, so the
+    un-normalised outputs sum_j 2^s_j v_j exceed 2^128 in every row: the
+    optimistic pass overflows float32 and must hand the rows to the exact pass
+    (weights <= 1), whose accumulators stay below keys * max|V|."""
+    wl = workload.Workload("t", 72, S=3, gh=9, gw=9, n_special=5, patch_begin=5, H=2)
+    q, k, v = wl.qkv_bf16()
+    qf, kf, vf = (workload.bf16_bits_to_f32(x) for x in (q, k, v))
+    qf[..., 63] = 256.0
+    kf[..., 63] = 2.8125
+    vf = vf * np.float32(2.0 ** VSHIFT)
+    q, k, v = (workload.f32_to_bf16_bits(x) for x in (qf, kf, vf))  # exact: powers of two and 8-bit values
+    if dtype == torch.float32:
+        q, k, v = (workload.bf16_bits_to_f32(x) for x in (q, k, v))
+    return wl, q, k, v
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_large_values_leave_the_optimistic_pass(dtype):
+    wl, q, k, v = _large_value_case(dtype)
+    S, T = wl.S, wl.T
+    # the case does what it says: row sums inside the bound, un-normalised outputs beyond float32
+    qf, kf, vf = (oracle.to_f64(x).reshape(S * T, 2, 64) for x in (q, k, v))
+    p = np.exp2(np.einsum("ihd,jhd->hij", qf, kf) * (MILD / np.log(2.0)))
+    assert np.log2(p.sum(-1)).max() < 100
+    assert (np.abs(np.einsum("hij,jhd->hid", p, vf)).max(-1) > 2.0 ** 128).all()
+    unit = 2.0 ** -VSHIFT
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    bf16 = dtype == torch.bfloat16
+    smax = _score_bound(q, k, S, T, True, MILD)
+    check = check_bf16 if bf16 else (lambda g, r, lab: _check_f32(g, r, lab, smax))
+    fo = to_f64(ffv.vggt_frame_attn(qd, kd, vd, scale=MILD))
+    check(fo * unit, oracle.frame_attn(q, k, v, S, T, scale=MILD) * unit, f"large V frame {dtype}")
+    ref = oracle.global_attn(q, k, v, S, T, scale=MILD) * unit
+    for splits in (1, 3):
+        go = to_f64(ffv.vggt_global_attn(qd, kd, vd, scale=MILD, kv_splits=splits))
+        check(go * unit, ref, f"large V global {dtype} splits={splits}")

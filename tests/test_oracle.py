@@ -658,3 +658,37 @@ def test_splitmix64_reference_outputs_and_normals():
     b = workload.f32_to_bf16_bits(np.array([1.0, 1.00390625, 1.01171875, -2.0, 3.0e-3], np.float32))
     # 1+2^-8 is a tie -> even (1.0); 1+3*2^-8 is a tie -> up to 1+2^-6
     np.testing.assert_array_equal(workload.bf16_bits_to_f32(b)[:4], [1.0, 1.0, 1.015625, -2.0])
+
+
+# --------------------------------------------------------------------------
+# Sensitivity of the GPU parity bars (tests/checks.py)
+# --------------------------------------------------------------------------
+
+def test_bf16_bars_see_a_lost_key_tile_at_full_size():
+    """Global attention at 32 frames of 518x518 (N = 43968, RoPE base 100), on
+    every 400th query row.  A result that lost the last 64-key tile, rounded to
+    bf16 like a kernel output, passes the absolute bars (max 2e-2, mean 2e-3)
+    but fails the scale-aware ones; the complete result rounded to bf16 passes
+    all of them."""
+    import checks
+
+    wl = workload.WORKLOADS["vggt-518-s32"]
+    q, k, v = wl.qkv_bf16()
+    H = wl.H
+    pos = np.tile(wl.positions(), (wl.S, 1))
+    qr = oracle.rope(q.reshape(wl.N, H, 64), pos, 100.0)
+    kr = oracle.rope(k.reshape(wl.N, H, 64), pos, 100.0)
+    vf = oracle.to_f64(v).reshape(wl.N, H, 64)
+    rows = np.arange(0, wl.N, 400)
+    ref = oracle.attention(qr, kr, vf, rows=rows)
+    lost = oracle.attention(qr, kr[:-64], vf[:-64], rows=rows)
+
+    def as_bf16(x):
+        return oracle.to_f64(workload.f32_to_bf16_bits(x.astype(np.float32))).reshape(x.shape)
+
+    e_lost = checks.bf16_errors(as_bf16(lost), ref)
+    e_full = checks.bf16_errors(as_bf16(ref), ref)
+    assert checks.bf16_absolute_ok(e_lost), e_lost  # the absolute bars alone accept it ...
+    assert not checks.bf16_ok(e_lost), e_lost  # ... the scale-aware bars reject it
+    assert e_lost["nrmse"] > 2 * checks.BF16_NRMSE, e_lost
+    assert checks.bf16_ok(e_full) and e_full["nrmse"] < 0.2 * checks.BF16_NRMSE, e_full
