@@ -6,10 +6,17 @@ passes raw device pointers and the current HIP stream, and raises on a
 non-OK status.  All computation happens in the library's HIP kernels; torch
 only provides device memory and streams.  There is no fallback: if the
 library is missing or fails to load, every call raises.
+
+Streams: a call launches on `stream` (default: torch's current stream) and,
+when one is given, runs with it as torch's current stream, so its workspace
+and default-allocated outputs belong to that stream.  Buffers the caller
+allocated elsewhere stay the caller's to order (Tensor.record_stream).
 """
 from __future__ import annotations
 
 import ctypes
+import functools
+import inspect
 import os
 
 import torch
@@ -137,6 +144,25 @@ def _pos(pos_yx, T: int):
     return ctypes.c_void_p(pos_yx.data_ptr())
 
 
+def _on_stream(fn):
+    """Run a call with the caller's `stream` as torch's current stream, so that the
+    workspace and any default-allocated outputs come from that stream's pool: the
+    caching allocator then hands a block freed after the call (the workspace) only
+    to later work of the same stream, never to another stream while the kernels
+    still read it."""
+    sig = inspect.signature(fn)
+
+    @functools.wraps(fn)
+    def wrapper(*args, **kwargs):
+        s = sig.bind_partial(*args, **kwargs).arguments.get("stream")
+        if s is None:
+            return fn(*args, **kwargs)
+        with torch.cuda.stream(s):
+            return fn(*args, **kwargs)
+
+    return wrapper
+
+
 def _workspace(nbytes: int, device, workspace):
     if nbytes == 0:
         return None, 0
@@ -151,6 +177,7 @@ def _workspace(nbytes: int, device, workspace):
 # the five calls (names as in the C ABI)
 # ---------------------------------------------------------------------------
 
+@_on_stream
 def vggt_attn_rope(x: torch.Tensor, pos_yx: torch.Tensor, rope_base: float = 100.0, stream=None) -> torch.Tensor:
     """Rotate x [S, T, H, 64] in place by 2D RoPE; returns x."""
     S, T, H = _tok(x, "x")
@@ -164,6 +191,7 @@ def vggt_frame_attn_workspace(S, T, H, rope_on, dtype=torch.bfloat16) -> int:
     return int(lib().vggt_frame_attn_workspace(S, T, H, int(rope_on), BF16 if dtype == torch.bfloat16 else F32))
 
 
+@_on_stream
 def vggt_frame_attn(q, k, v, out=None, pos_yx=None, rope_base=100.0, scale=0.0, workspace=None, stream=None):
     """Frame-wise attention over [S, T, H, 64]; returns out."""
     S, T, H = _tok(q, "q")
@@ -187,6 +215,7 @@ def vggt_global_attn_workspace(S, T, H, kv_splits, rope_on, dtype=torch.bfloat16
                                                 BF16 if dtype == torch.bfloat16 else F32))
 
 
+@_on_stream
 def vggt_global_attn(q, k, v, out=None, pos_yx=None, rope_base=100.0, scale=0.0, kv_splits=0, workspace=None,
                      stream=None):
     """Global attention over all S*T tokens; returns out."""
@@ -227,6 +256,7 @@ def _check_qkv(q, k, v, out):
     return S, T, H, out
 
 
+@_on_stream
 def vggt_frame_attn_qknorm(q, k, v, q_norm, k_norm, eps=1e-5, out=None, pos_yx=None, rope_base=100.0, scale=0.0,
                            workspace=None, stream=None):
     """Frame-wise attention with per-head LayerNorm of q and k (gamma, beta pairs) before RoPE."""
@@ -242,6 +272,7 @@ def vggt_frame_attn_qknorm(q, k, v, q_norm, k_norm, eps=1e-5, out=None, pos_yx=N
     return out
 
 
+@_on_stream
 def vggt_global_attn_qknorm(q, k, v, q_norm, k_norm, eps=1e-5, out=None, pos_yx=None, rope_base=100.0, scale=0.0,
                             kv_splits=0, workspace=None, stream=None):
     """Global attention with per-head LayerNorm of q and k (gamma, beta pairs) before RoPE."""
@@ -265,6 +296,7 @@ def _norm_arg(q_norm, k_norm, eps, H):
     return ctypes.byref(_qk_norm(q_norm, k_norm, eps, H)), PRE_QKNORM
 
 
+@_on_stream
 def vggt_frame_attn_ex(q, k, v, T_active, out=None, pos_yx=None, rope_base=100.0, scale=0.0, q_norm=None,
                        k_norm=None, eps=1e-5, workspace=None, stream=None):
     """Frame attention over the first T_active tokens of each frame of [S, T, H, 64];
@@ -280,6 +312,7 @@ def vggt_frame_attn_ex(q, k, v, T_active, out=None, pos_yx=None, rope_base=100.0
     return out
 
 
+@_on_stream
 def vggt_global_attn_ex(q, k, v, T_active, xq=None, xk=None, xv=None, out=None, xout=None, pos_yx=None,
                         rope_base=100.0, scale=0.0, kv_splits=0, q_norm=None, k_norm=None, eps=1e-5,
                         workspace=None, stream=None):
@@ -304,6 +337,7 @@ def vggt_global_attn_ex(q, k, v, T_active, xq=None, xk=None, xv=None, out=None, 
     return out, (xout if E else None)
 
 
+@_on_stream
 def vggt_frame_attn_train(q, k, v, out=None, lse=None, pos_yx=None, rope_base=100.0, scale=0.0, workspace=None,
                           stream=None):
     """Frame attention that also returns the log-normaliser lse [S*T, H] (float32); returns (out, lse)."""
@@ -317,6 +351,7 @@ def vggt_frame_attn_train(q, k, v, out=None, lse=None, pos_yx=None, rope_base=10
     return out, lse
 
 
+@_on_stream
 def vggt_global_attn_train(q, k, v, out=None, lse=None, pos_yx=None, rope_base=100.0, scale=0.0, kv_splits=0,
                            workspace=None, stream=None):
     """Global attention that also returns the log-normaliser lse [S*T, H] (float32); returns (out, lse)."""
@@ -346,6 +381,7 @@ def _backward(name, global_, q, k, v, out, dout, lse, pos_yx, rope_base, scale, 
     return dq, dk, dv
 
 
+@_on_stream
 def vggt_frame_attn_backward(q, k, v, out, dout, lse, pos_yx=None, rope_base=100.0, scale=0.0, workspace=None,
                              stream=None, grads=None):
     """Gradients (dq, dk, dv) of frame attention from the training forward's out and lse."""
@@ -353,6 +389,7 @@ def vggt_frame_attn_backward(q, k, v, out, dout, lse, pos_yx=None, rope_base=100
                      stream, grads)
 
 
+@_on_stream
 def vggt_global_attn_backward(q, k, v, out, dout, lse, pos_yx=None, rope_base=100.0, scale=0.0, workspace=None,
                               stream=None, grads=None):
     """Gradients (dq, dk, dv) of global attention from the training forward's out and lse."""
@@ -364,6 +401,7 @@ def vggt_descriptor_count(T, gh, gw, ph, pw) -> int:
     return int(lib().vggt_descriptor_count(T, gh, gw, ph, pw))
 
 
+@_on_stream
 def vggt_descriptor_pool(k, v, gh, gw, patch_begin, ph=2, pw=2, kd=None, vd=None, stream=None):
     """Pool K and V [S, T, H, 64] into descriptors [S, Dn, H, 64]; returns (kd, vd)."""
     S, T, H = _tok(k, "k")
@@ -387,6 +425,7 @@ def vggt_descriptor_xattn_workspace(S, T, Dn, H, kv_splits, dtype=torch.bfloat16
     return int(lib().vggt_descriptor_xattn_workspace(S, T, Dn, H, kv_splits, BF16 if dtype == torch.bfloat16 else F32))
 
 
+@_on_stream
 def vggt_descriptor_xattn(q, kd, vd, out=None, scale=0.0, kv_splits=0, workspace=None, stream=None):
     """All S*T queries attend to all S*Dn descriptors; returns out."""
     S, T, H = _tok(q, "q")
@@ -420,6 +459,7 @@ def vggt_descriptor_cache_bytes(capacity: int, H: int, dtype=torch.bfloat16) -> 
     return int(lib().vggt_descriptor_cache_bytes(capacity, H, _code(dtype)))
 
 
+@_on_stream
 def vggt_descriptor_cache_append(cache: torch.Tensor, capacity: int, H: int, used: int, kd: torch.Tensor,
                                  vd: torch.Tensor, dtype=None, stream=None) -> int:
     """Append descriptors kd/vd [..., H, 64] (flattened to [n, H, 64]) at position `used` of the
@@ -441,6 +481,7 @@ def vggt_descriptor_cache_attn_workspace(nq: int, used: int, H: int, kv_splits: 
     return int(lib().vggt_descriptor_cache_attn_workspace(nq, used, H, kv_splits, _code(dtype)))
 
 
+@_on_stream
 def vggt_descriptor_cache_attn(q: torch.Tensor, cache: torch.Tensor, capacity: int, used: int, out=None, scale=0.0,
                                kv_splits=0, workspace=None, stream=None) -> torch.Tensor:
     """Query tokens q [..., H, 64] attend to the first `used` cached descriptors; returns out (q's shape)."""
@@ -459,6 +500,7 @@ def vggt_descriptor_cache_attn(q: torch.Tensor, cache: torch.Tensor, capacity: i
     return out
 
 
+@_on_stream
 def vggt_descriptor_chunked_xattn(q: torch.Tensor, cache: torch.Tensor, capacity: int, Dn: int, chunk_frames: int,
                                   out=None, scale=0.0, stream=None) -> torch.Tensor:
     """All chunks in one launch: q [S, T, H, 64]; the cache holds the S*Dn descriptors of all frames."""

@@ -32,7 +32,7 @@ vggt_status fail(vggt_status s, const char* fmt, ...) {
 constexpr int kMaxHeads = 128;
 constexpr int64_t kMaxTokens = int64_t(1) << 28;
 constexpr int kMaxSplits = 64;
-constexpr int kAssumedCUs = 256;       // MI355X; used only to size the key split
+constexpr int kDefaultCUs = 256;  // MI355X; the split plan's CU count if the device cannot be queried
 
 // ---- device check, cached per device (read-only after first use)
 struct DevInfo {
@@ -62,6 +62,22 @@ vggt_status check_device() {
   return VGGT_OK;
 }
 
+// CU count of the current device (cached with the device check); sizes the key split
+int current_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kDefaultCUs;
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  DevInfo& d = g_dev[dev];
+  if (!d.checked) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return kDefaultCUs;
+    d.gfx950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    d.cus = prop.multiProcessorCount;
+    d.checked = true;
+  }
+  return d.cus > 0 ? d.cus : kDefaultCUs;
+}
+
 size_t elem_size(vggt_dtype dt) { return dt == VGGT_F32 ? 4 : 2; }
 bool dtype_ok(vggt_dtype dt) { return dt == VGGT_BF16 || dt == VGGT_F32; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -77,8 +93,8 @@ bool tokens_ok(int S, int T, int H) {
   return (int64_t)S * T < kMaxTokens;
 }
 
-// ---- key-split plan (a pure function of the shape, shared by the workspace
-//      queries and the calls)
+// ---- key-split plan (a function of the shape and the current device's CU
+//      count, shared by the workspace queries and the calls)
 struct SplitPlan {
   int splits;
   int keys_per_split;
@@ -105,7 +121,7 @@ SplitPlan plan_splits(int64_t nq, int64_t nk, int H, int requested, vggt_dtype d
     // resident workgroups per CU: the bf16 kernel's declared occupancy; the untuned fp32
     // debug kernel is planned with the same two
     const int per_cu = dt == VGGT_F32 ? 2 : vggt::attn_bf16_workgroups_per_cu();
-    const int64_t slots = (int64_t)kAssumedCUs * per_cu;
+    const int64_t slots = (int64_t)current_cus() * per_cu;
     double best = 1e300;
     for (int s = 1; s <= kMaxSplits && s <= ktiles; ++s) {
       const double rounds = (double)(wg * s) / (double)slots;

@@ -24,8 +24,10 @@
  *
  * Conventions for every call:
  *   - Ownership: the caller owns all device buffers, including the workspace
- *     sized by the matching *_workspace() query.  The library never allocates,
- *     frees or synchronises.
+ *     sized by the matching *_workspace() query.  The compute calls never
+ *     allocate, free or synchronise.  The diagnostic kernel timer is the one
+ *     exception: vggt_timer_start creates HIP events (2 per armed launch) and
+ *     vggt_timer_stop waits for them and destroys them.
  *   - Streams: `stream` is a hipStream_t passed as void*; NULL means the null
  *     stream.  Work is enqueued asynchronously on it.
  *   - Errors: arguments are validated on the host before anything is
@@ -44,12 +46,17 @@
  *     exception is vggt_global_attn_ex with n_extra > 0 and S = 0, which is
  *     VGGT_ERR_SHAPE.
  *   - Running time (bf16 forward calls): the kernel first computes every
- *     row's softmax against a fixed reference and checks each row's sum at
- *     the end.  A workgroup with a row outside the range recomputes its 256
- *     rows exactly, taking up to about 2.4x the usual time.  Such a row has a
- *     largest logit above about 50 or all logits below about -40 (natural
- *     units, scale included).  Results are the same softmax either way, up to
+ *     row's softmax against a fixed reference and checks, at the end, each
+ *     row's sum and that its un-normalised output stayed finite.  A workgroup
+ *     with a row outside the range recomputes its 256 rows exactly, taking up
+ *     to about 2.4x the usual time.  Such a row has a largest logit above
+ *     about 50 or all logits below about -40 (natural units, scale included),
+ *     or large values: weights up to 2^100 times |V| overflow float32 once
+ *     |V| exceeds about 2^28.  Results are the same softmax either way, up to
  *     rounding.
+ *   - Value range: the exact recomputation keeps every weight in (0, 1], so
+ *     its float32 accumulators hold at most (keys) * max|V|; outputs are
+ *     finite and exact up to rounding for max|V| * keys below 2^127.
  */
 #ifndef VGGT_ATTN_H
 #define VGGT_ATTN_H
@@ -156,7 +163,9 @@ vggt_status vggt_frame_attn_qknorm(const void* q, const void* k, const void* v, 
  * position for RoPE (frames carry no index of their own).
  *   Arguments as for vggt_frame_attn, plus
  *   kv_splits  number of key ranges computed by separate workgroups and merged
- *              exactly by log-sum-exp; 0 lets the library choose (1..64).
+ *              exactly by log-sum-exp; 0 lets the library choose (1..64) from
+ *              the shape and the current device's CU count, so a workspace
+ *              query and its call must see the same current device.
  */
 size_t vggt_global_attn_workspace(int S, int T, int H, int kv_splits, int rope_on, vggt_dtype dt);
 vggt_status vggt_global_attn(const void* q, const void* k, const void* v, void* o, vggt_dtype dt, int S, int T,
