@@ -51,6 +51,7 @@ SIGNATURES = {
     "vggt_attn_rope": (_i, [_vp, _i, _i, _i, _i, _vp, _f, _vp]),
     "vggt_frame_attn_workspace": (_sz, [_i, _i, _i, _i, _i]),
     "vggt_frame_attn": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _f, _f, _vp, _sz, _vp]),
+    "vggt_frame_attn_noalloc": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _f, _f, _vp]),
     "vggt_global_attn_workspace": (_sz, [_i, _i, _i, _i, _i, _i]),
     "vggt_global_attn": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _f, _f, _i, _vp, _sz, _vp]),
     "vggt_frame_attn_qknorm": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _f, _f, _np, _vp, _sz, _vp]),
@@ -213,6 +214,17 @@ def vggt_global_attn_workspace(S, T, H, kv_splits, rope_on, dtype=torch.bfloat16
     """rope_on: bool, or PRE_ROPE | PRE_QKNORM flags."""
     return int(lib().vggt_global_attn_workspace(S, T, H, kv_splits, int(rope_on),
                                                 BF16 if dtype == torch.bfloat16 else F32))
+
+
+@_on_stream
+def vggt_frame_attn_noalloc(q, k, v, out=None, pos_yx=None, rope_base=100.0, scale=0.0, stream=None):
+    """vggt_frame_attn whose workspace is the library's own device array (the C call
+    allocates nothing; pass `out` to allocate nothing here either); returns out."""
+    S, T, H, out = _check_qkv(q, k, v, out)
+    _check("vggt_frame_attn_noalloc",
+           lib().vggt_frame_attn_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _dtype_code(q), S, T, H,
+                                         _pos(pos_yx, T), rope_base, scale, _stream(stream)))
+    return out
 
 
 @_on_stream

@@ -495,6 +495,54 @@ VGGT_API vggt_status vggt_frame_attn(const void* q, const void* k, const void* v
   return frame_attn(q, k, v, o, dt, S, T, H, pos_yx, rope_base, scale, nullptr, workspace, ws_bytes, stream);
 }
 
+// ---- allocation-free frame attention: the workspace lives in a file-scope device
+//      array of kNoallocScratchBytes, shared by every call on a device.  In host code
+//      `scratch` is only a stand-in for the symbol: its device address is looked up
+//      once per device with hipGetSymbolAddress and only that address is used.
+namespace {
+
+constexpr size_t kNoallocScratchBytes = VGGT_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) char scratch[kNoallocScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch[64];  // device address of `scratch` per device index, null until looked up
+
+vggt_status scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(VGGT_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(VGGT_ERR_DEVICE, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return device_error("hipGetSymbolAddress(scratch)", e != hipSuccess ? e : hipErrorUnknown);
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return VGGT_OK;
+}
+
+}  // namespace
+
+VGGT_API vggt_status vggt_frame_attn_noalloc(const void* q, const void* k, const void* v, void* o, vggt_dtype dt,
+                                             int S, int T, int H, const int32_t* pos_yx, float rope_base,
+                                             float scale, void* stream) {
+  g_last_error[0] = 0;
+  if (!dtype_ok(dt)) return fail(VGGT_ERR_UNSUPPORTED, "unknown dtype %d", (int)dt);
+  if (!tokens_ok(S, T, H)) return fail(VGGT_ERR_SHAPE, "bad shape S=%d T=%d H=%d", S, T, H);
+  if (S == 0) return VGGT_OK;
+  const size_t need = vggt_frame_attn_workspace(S, T, H, pos_yx != nullptr, dt);
+  if (need > kNoallocScratchBytes)
+    return fail(VGGT_ERR_WORKSPACE, "this shape needs %zu bytes of scratch; the allocation-free call has %zu", need,
+                kNoallocScratchBytes);
+  const size_t bytes = (size_t)S * T * H * vggt::kHeadDim * elem_size(dt);
+  if (vggt_status s = validate_attn({q, k, v, o}, pos_yx, rope_base, 0, nullptr, 0, bytes, bytes)) return s;
+  if (vggt_status s = check_device()) return s;
+  void* ws = nullptr;
+  if (vggt_status s = scratch_address(&ws)) return s;
+  return frame_attn(q, k, v, o, dt, S, T, H, pos_yx, rope_base, scale, nullptr, ws, kNoallocScratchBytes, stream);
+}
+
 VGGT_API vggt_status vggt_frame_attn_qknorm(const void* q, const void* k, const void* v, void* o, vggt_dtype dt,
                                             int S, int T, int H, const int32_t* pos_yx, float rope_base, float scale,
                                             const vggt_qk_norm* norm, void* workspace, size_t ws_bytes,

@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define VGGT_ATTN_ABI_VERSION 5
+#define VGGT_ATTN_ABI_VERSION 6
 #define VGGT_HEAD_DIM 64
 
 typedef enum {
@@ -149,6 +149,24 @@ size_t vggt_frame_attn_workspace(int S, int T, int H, int rope_on, vggt_dtype dt
 vggt_status vggt_frame_attn(const void* q, const void* k, const void* v, void* o, vggt_dtype dt, int S, int T,
                             int H, const int32_t* pos_yx, float rope_base, float scale, void* workspace,
                             size_t ws_bytes, void* stream);
+
+/*
+ * vggt_frame_attn without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, results and errors as
+ * vggt_frame_attn; the workspace is a library-owned device array of
+ * VGGT_NOALLOC_SCRATCH_BYTES on each device that calls it, held until the
+ * process ends.  The call itself allocates, frees and synchronises nothing.
+ *   Limit: vggt_frame_attn_workspace(S, T, H, pos_yx != NULL, dt) must not
+ *   exceed VGGT_NOALLOC_SCRATCH_BYTES, else VGGT_ERR_WORKSPACE before anything
+ *   is enqueued (bf16 with RoPE: S * H * ceil(T / 64) <= about 4000, e.g. 8
+ *   frames of 1374 tokens x 16 heads).
+ *   Every call on one device uses the same array: calls that may overlap on
+ *   one device (different streams without ordering) race; order them.
+ */
+#define VGGT_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+vggt_status vggt_frame_attn_noalloc(const void* q, const void* k, const void* v, void* o, vggt_dtype dt, int S,
+                                    int T, int H, const int32_t* pos_yx, float rope_base, float scale, void* stream);
 /* The same with the Q/K LayerNorm prologue (norm: host pointer, NULL = none;
  * the workspace is sized with rope_on = VGGT_PRE_QKNORM | (RoPE ? VGGT_PRE_ROPE : 0)).
  * VGGT_ERR_NULL if a parameter array is NULL, VGGT_ERR_SHAPE if eps <= 0,

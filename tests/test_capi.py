@@ -32,7 +32,7 @@ def L():
 
 def test_exports_match_header(L):
     declared = header_functions()
-    assert len(declared) == 30
+    assert len(declared) == 31
     out = subprocess.run(["nm", "-D", "--defined-only", ffv.LIB_PATH], capture_output=True, text=True,
                          check=True).stdout
     exported = sorted(set(m for m in re.findall(r"\bT (vggt_\w+)", out)))
@@ -41,7 +41,7 @@ def test_exports_match_header(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.vggt_abi_version() == 5
+    assert L.vggt_abi_version() == 6
     for code, name in ffv.STATUS.items():
         assert L.vggt_status_str(code).decode() == name
     assert L.vggt_status_str(99).decode() == "VGGT_ERR_UNKNOWN"
@@ -308,3 +308,22 @@ def test_empty_calls_are_noops(L):
         assert L.vggt_global_attn_ex(None, None, None, None, dt, 0, 8, 6, 1, X, X, X, X, 2, None, 100.0, 0.0, 0,
                                      None, None, 0, None) == SHAPE
         assert L.vggt_global_attn_ex_workspace(0, 8, 6, 2, 1, 0, 1, dt) == 0
+
+
+def test_noalloc_frame_attn_arguments(L):
+    """The allocation-free frame attention rejects, before touching the device,
+    shapes whose workspace exceeds its scratch array and the usual bad arguments."""
+    f = L.vggt_frame_attn_noalloc
+    p = ctypes.c_void_p(1 << 20)
+    pos = ctypes.c_void_p(1 << 21)
+    limit = 64 << 20
+    assert L.vggt_frame_attn_workspace(8, 1374, 16, 1, 0) <= limit
+    assert L.vggt_frame_attn_workspace(32, 1374, 16, 1, 0) > limit
+    assert f(p, p, p, p, 0, 32, 1374, 16, pos, 100.0, 0.0, None) == WS
+    assert f(p, p, p, p, 1, 8, 1374, 16, pos, 100.0, 0.0, None) == WS  # fp32 rotated copies: 90 MB
+    assert f(p, p, p, p, 2, 8, 1374, 16, None, 100.0, 0.0, None) == UNSUP
+    assert f(p, p, p, p, 0, 8, 0, 16, None, 100.0, 0.0, None) == SHAPE
+    assert f(None, p, p, p, 0, 8, 1374, 16, None, 100.0, 0.0, None) == NULL
+    assert f(ctypes.c_void_p((1 << 20) + 8), p, p, ctypes.c_void_p(1 << 30), 0, 8, 1374, 16, None, 100.0, 0.0,
+             None) == ALIGN
+    assert f(None, None, None, None, 0, 0, 1374, 16, None, 100.0, 0.0, None) == OK  # empty call
