@@ -11,9 +11,12 @@ tokens per frame, N = 43968, 16 heads of 64, bf16, 2D RoPE base 100):
 
 FLOP = 4 * Nq * Nk * H * 64 (QK^T plus PV, 2 flop per multiply-add).  Inputs
 are seeded N(0,1) bf16 tensors already resident in HBM.  `value` is the
-step's algorithmic attention TFLOP/s over the timed region; per-call times
-come from HIP events recorded on the launch stream.  The oracle (float64, CPU)
-is timed on a row sample of the same step as the CPU baseline.
+metric: global-attention TFLOP/s, the global call's FLOP over its mean
+duration within the timed steps (the whole call: RoPE table, K/V tile passes,
+attention kernel and any split merge); `step_tflops` is all of the step's
+attention FLOP over the step time.  Per-call times come from HIP events
+recorded on the launch stream.  The oracle (float64, CPU) is timed on a row
+sample of the same step as the CPU baseline.
 """
 from __future__ import annotations
 
@@ -34,14 +37,14 @@ METRIC = "global-attention TFLOP/s + ms/layer at S frames; % of bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 
-# HBM traffic of one global-attention kernel launch on this workload, from
-# rocprofv3 FETCH_SIZE / WRITE_SIZE runs scaled by the counters' reading on a
-# plain 1 GiB copy (profiles/attn_fwd_bf16_vggt-518-s32_counters.md).  Valid
-# only for the kernel source it was measured on.
+# HBM traffic of one global-attention kernel launch per workload, from rocprofv3
+# FETCH_SIZE / WRITE_SIZE runs scaled by the counters' reading on a plain 1 GiB
+# copy (profiles/attn_fwd_bf16_*_counters.md): (read bytes, written bytes).
+# Valid only for the kernel source the counters were taken on.
 PROFILED_TRAFFIC = {
-    "kernel_source_sha256": "e6a55327223a6be9acfa0f0dc1cc3ab4b01c087497cf5d08aa66ace99a996c78",
-    "read_bytes": 1175.2e6,
-    "write_bytes": 90.0e6,
+    "kernel_source_sha256": "cc19ac10dec27610f2f9d485e6d9fc85e3f5e1869750b040a6c5dd92e0e03885",
+    "vggt-518-s32": (1166.7e6, 90.0e6),
+    "omega-512-s64": (2930.7e6, 920.1e6),
 }
 
 
@@ -49,8 +52,9 @@ def attn_flops(nq: int, nk: int, H: int = 16, d: int = 64) -> float:
     return 4.0 * nq * nk * H * d
 
 
-def profiled_traffic():
-    """Bytes per launch if the attention kernel is the one the counters were taken on, else None."""
+def kernel_source_sha256():
+    """Hash of the attention kernel's source and of the header that fixes its LDS tile
+    layout, without comments and blank lines, or None if they cannot be read."""
     import hashlib
 
     # the kernel's source and the header that fixes its LDS tile layout, without comments
@@ -65,10 +69,15 @@ def profiled_traffic():
                         h.update(code.encode() + b"\n")
     except OSError:
         return None
-    sha = h.hexdigest()
-    if sha != PROFILED_TRAFFIC["kernel_source_sha256"]:
+    return h.hexdigest()
+
+
+def profiled_traffic(workload_name="vggt-518-s32"):
+    """HBM bytes per global-attention launch on a workload if the kernel is the one the
+    counters were taken on, else None."""
+    if workload_name not in PROFILED_TRAFFIC or kernel_source_sha256() != PROFILED_TRAFFIC["kernel_source_sha256"]:
         return None
-    return PROFILED_TRAFFIC["read_bytes"] + PROFILED_TRAFFIC["write_bytes"]
+    return sum(PROFILED_TRAFFIC[workload_name])
 
 
 def main() -> int:
@@ -184,7 +193,9 @@ def main() -> int:
     }
     step_flops = sum(flops.values())
     ms_per_step = elapsed * 1e3 / args.steps
-    value = step_flops / (ms_per_step * 1e-3) / 1e12
+    step_tflops = step_flops / (ms_per_step * 1e-3) / 1e12
+    g_call_ms = float(np.mean(per_call["global"]))
+    value = flops["global"] / (g_call_ms * 1e-3) / 1e12
     g_tflops = flops["global"] / (med["global"] * 1e-3) / 1e12
     g_kernel_ms = float(np.mean(kernel_ms["global"]))
     g_kernel_tflops = flops["global"] / (g_kernel_ms * 1e-3) / 1e12
@@ -209,12 +220,15 @@ def main() -> int:
                         f"2x2 descriptor pool + descriptor cross-attention ({S * Dn} descriptors)",
             "S": S, "T": T, "N": N, "H": H, "head_dim": 64,
         },
+        "value_definition": "global attention: 4*N^2*H*64 flop / mean duration of the vggt_global_attn call "
+                            "within the timed steps (HIP events on its stream)",
+        "step_tflops": round(step_tflops, 2),
         "ms_per_layer": round(med["frame"] + med["global"], 4),
         "calls_ms_median": {c: round(x, 4) for c, x in med.items()},
         "calls_ms_p10_p90": {c: [round(float(np.percentile(x, 10)), 4), round(float(np.percentile(x, 90)), 4)]
                              for c, x in per_call.items()},
-        "global_attention_tflops": round(g_tflops, 2),
-        "global_frac_of_bf16_peak": round(g_tflops / PEAK_BF16_TFLOPS, 4),
+        "global_attention_tflops_median_call": round(g_tflops, 2),
+        "global_frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "frame_attention_tflops": round(flops["frame"] / (med["frame"] * 1e-3) / 1e12, 2),
         "xattn_tflops": round(flops["xattn"] / (med["xattn"] * 1e-3) / 1e12, 2),
         "pool_gbs": round(pool_bytes / (med["pool"] * 1e-3) / 1e9, 1),
@@ -250,7 +264,7 @@ def main() -> int:
         result["cpu_baseline"], result["parity_sample"] = cpu_baseline(wl, q, k, v, pos, Dn, ph, pw, go, fo, xo,
                                                                        args.cpu_row_stride)
         # throughput ratio of the step on the GPU to the oracle on the host's cores
-        result["gpu_over_cpu_oracle"] = round(value / result["cpu_baseline"]["value"], 1)
+        result["gpu_over_cpu_oracle"] = round(step_tflops / result["cpu_baseline"]["value"], 1)
     print(json.dumps(result), flush=True)
     return 0
 
@@ -519,6 +533,17 @@ def bench_omega(ffv, dev, iters):
         res[f"{name}_kernel_tflops"] = round(flops[name] / (kernel_ms * 1e-3) / 1e12, 2)
         res[f"{name}_kernel_frac_of_bf16_peak"] = round(flops[name] / (kernel_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
     res["ms_per_layer"] = round(res["frame_call_ms"] + res["global_call_ms"], 4)
+    g = flops["global"] / (res["global_kernel_ms"] * 1e-3) / 1e12
+    res["roofline"] = {
+        "kernel": f"attn_fwd_bf16_kernel, global attention launch ({S * T} x {S * T} tokens, {H} heads of 64); "
+                  f"4*N*N*H*64 flop per launch / mean kernel time from HIP events on its stream",
+        "bound": "mfma",
+        "achieved": round(g, 2),
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(g / PEAK_BF16_TFLOPS, 4),
+        "traffic": profiled_traffic("omega-512-s64"),
+    }
     return res
 
 
@@ -621,10 +646,22 @@ def bench_stream(ffv, dev, passes, warmup, chunk_frames=10):
     }
 
 
+def _cpu_model():
+    """The host CPU's model name from /proc/cpuinfo, or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(wl, q, k, v, pos, Dn, ph, pw, go, fo, xo, stride):
     """The float64 oracle, untuned, on every `stride`-th query row of each
-    attention call of the step (plus the pooling of those rows' frames is not
-    needed: the oracle pools all frames), timed on the host cores."""
+    attention call of the step, plus the pooling of every frame (the
+    cross-attention rows need all descriptors), timed on the host cores."""
     import torch
 
     import oracle
@@ -644,6 +681,8 @@ def cpu_baseline(wl, q, k, v, pos, Dn, ph, pw, go, fo, xo, stride):
         "value": round(sampled_flops / secs / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": nthreads,
+        "host_threads": os.cpu_count(),
+        "cpu_model": _cpu_model(),
         "kind": "oracle",
         "sample": f"every {stride}th query row ({rows.size} of {N}) of frame, global and descriptor attention, "
                   f"all heads, plus full descriptor pooling; {secs:.1f} s",
@@ -655,7 +694,9 @@ def cpu_baseline(wl, q, k, v, pos, Dn, ph, pw, go, fo, xo, stride):
     par = {}
     for name, got, ref in (("frame", fo, ref_f), ("global", go, ref_g), ("xattn", xo, ref_x)):
         err = np.abs(host(got) - ref.reshape(rows.size, H, 64))
-        par[name] = {"max_abs": float(err.max()), "mean_abs": float(err.mean())}
+        r = ref.reshape(rows.size, H, 64)
+        par[name] = {"max_abs": float(err.max()), "mean_abs": float(err.mean()),
+                     "nrmse": float(np.sqrt(np.mean(err ** 2)) / np.sqrt(np.mean(r ** 2)))}
     return base, par
 
 
