@@ -188,6 +188,13 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
     rest /= p.nseq;
     split = rest % p.splits;
     head = rest / p.splits;
+  } else if (p.k_seq_stride == 0) {
+    // sequences sharing one key set: each XCD's contiguous range holds one head's
+    // (and key split's) work over all sequences, so its L2 streams that head's keys only
+    seq = rest % p.nseq;
+    rest /= p.nseq;
+    split = rest % p.splits;
+    head = rest / p.splits;
   } else {
     head = rest % p.H;
     rest /= p.H;
