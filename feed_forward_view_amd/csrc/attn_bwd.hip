@@ -218,17 +218,24 @@ void attn_bwd_dq_kernel(AttnBwdProblem p) {
 #pragma unroll
       for (int db = 0; db < 4; ++db) ktf[c][db] = read_tr_a(sm.k[stage], c, db, lane);
     const bool tail = t == p.ntile - 1 && 64 * p.ntile > p.n;
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      // S^T and dP^T of this query block: lane holds keys 16kb + 4g + r of its query
-      f32x4 s[4], dp[4];
+    // S^T and dP^T of a query block (lane holds keys 16kb + 4g + r of its query), and
+    // dS^T = P dP^T as the bf16 B operand of dQ^T += K^T dS^T for 32-key chunk c.  The tile is
+    // four phases, so that each block's exponentials, products and packs run beside the
+    // other block's independent MFMAs:  S,dP(0) | S,dP(1) + dS(0) | dQ(0) + dS(1) | dQ(1)
+    f32x4 s[2][4], dp[2][4];
+    auto sdp = [&](int qb) {
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        s[kb] = mfma16(kf[kb][0], qf[qb][0], nl[qb]);
-        s[kb] = mfma16(kf[kb][1], qf[qb][1], s[kb]);
-        dp[kb] = mfma16(vf[kb][0], df[qb][0], nd[qb]);
-        dp[kb] = mfma16(vf[kb][1], df[qb][1], dp[kb]);
+        s[qb][kb] = mfma16(kf[kb][0], qf[qb][0], nl[qb]);
+        dp[qb][kb] = mfma16(vf[kb][0], df[qb][0], nd[qb]);
       }
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        s[qb][kb] = mfma16(kf[kb][1], qf[qb][1], s[qb][kb]);
+        dp[qb][kb] = mfma16(vf[kb][1], df[qb][1], dp[qb][kb]);
+      }
+    };
+    auto mask = [&](int qb) {
       if (tail) {
         // keys past the end are zero rows, so their score would be the bare
         // -lse2, whose exponential overflows when the row's log-normaliser lies
@@ -237,22 +244,51 @@ void attn_bwd_dq_kernel(AttnBwdProblem p) {
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            if (64 * t + 16 * kb + 4 * g + r >= p.n) s[kb][r] = -INFINITY;
+            if (64 * t + 16 * kb + 4 * g + r >= p.n) s[qb][kb][r] = -INFINITY;
       }
-      // dS^T = P dP^T as the bf16 B operand of dQ^T += K^T dS^T, chunk by chunk of 32 keys
+    };
+    auto dsw = [&](int qb, int c) {
+      u32x4 w;
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        u32x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int kb = 2 * c + (e >> 1), r = 2 * (e & 1);
-          w[e] = pack_bf16x2(__builtin_amdgcn_exp2f(s[kb][r]) * dp[kb][r],
-                             __builtin_amdgcn_exp2f(s[kb][r + 1]) * dp[kb][r + 1]);
-        }
-#pragma unroll
-        for (int db = 0; db < 4; ++db) acc[qb][db] = mfma16(ktf[c][db], as_bf16x8(w), acc[qb][db]);
+      for (int e = 0; e < 4; ++e) {
+        const int kb = 2 * c + (e >> 1), r = 2 * (e & 1);
+        w[e] = pack_bf16x2(__builtin_amdgcn_exp2f(s[qb][kb][r]) * dp[qb][kb][r],
+                           __builtin_amdgcn_exp2f(s[qb][kb][r + 1]) * dp[qb][kb][r + 1]);
       }
+      return w;
+    };
+    auto dq = [&](int qb, const u32x4 (&w)[2]) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int db = 0; db < 4; ++db) acc[qb][db] = mfma16(ktf[c][db], as_bf16x8(w[c]), acc[qb][db]);
+    };
+    u32x4 w0[2], w1[2];
+    sdp(0);
+    mask(0);
+    __builtin_amdgcn_sched_barrier(0);
+    sdp(1);
+    w0[0] = dsw(0, 0);
+    w0[1] = dsw(0, 1);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x400, 1, 0);  // exponential
+      __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);  // other VALU
     }
+    __builtin_amdgcn_sched_barrier(0);
+    mask(1);
+    dq(0, w0);
+    w1[0] = dsw(1, 0);
+    w1[1] = dsw(1, 1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x400, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    dq(1, w1);
   }
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
