@@ -26,7 +26,7 @@
 // units.  The score registers of key blocks 2c and 2c+1 are, in order, the
 // bf16 B operand of the P V product for 32-key chunk c: that operand's key
 // index 8g + i stands for key 4g + i (i < 4) or 16 + 4g + i - 4 of the chunk,
-// and the V^T tiles store their keys in that order.
+// and the V^T operand must hold its keys in that order (see Operands).
 //
 // Why 16x16x32: under sustained load this chip holds its clock with the
 // 16x16x32 shape where the 32x32x16 shape runs into the power limit.
@@ -52,15 +52,25 @@
 // slow path moves m (rescaling O and l exactly by 2^(m_old - m_new)) and
 // redoes the block.  The final O / l is the same softmax whatever m is.
 //
-// Operands.  A pre-pass lays K (rotated when RoPE is on) and V^T out in
-// tiles of 64 keys, each tile 8 KiB in exactly the order the LDS tile uses
-// (K rows in key order, V^T rows holding each 32-key chunk in the operand
-// order above, 16-byte units XOR-swizzled per row so that the 16 lanes of an
-// operand read hit distinct banks; keys past the end are zero).  Tiles are
-// then copied linearly into a 4-stage LDS ring with global_load_lds_dwordx4,
-// three tiles ahead of use; one barrier per tile.  The last (partial) tile of
-// a key range is peeled out of the loop and its missing keys are masked to
-// -inf.
+// Operands.  A pre-pass lays K (rotated when RoPE is on) out in tiles of 64
+// keys, each tile 8 KiB in exactly the order the LDS tile uses (rows in key
+// order, 16-byte units XOR-swizzled per row so that the lanes of an operand
+// read hit distinct banks; keys past the end are zero), and the tiles are
+// copied linearly into a 4-stage LDS ring with global_load_lds_dwordx4, three
+// tiles ahead of use; one barrier per tile.  V comes in one of two forms:
+//   V^T tiles   a second pre-pass writes V^T tiles whose rows hold each 32-key
+//               chunk in the operand order above; eight ds_read_b128 per tile
+//               and wave read the operand;
+//   V in place  the copies gather V rows straight from the [token][head][64]
+//               tensor into a row tile laid out as the K tile (each lane
+//               fetches the 16-byte unit that its LDS slot holds; rows past the
+//               key range arrive as zeros), and sixteen transposing reads
+//               (ds_read_b64_tr_b16) per tile and wave form the operand.
+// The transposing form saves the V pre-pass (one read and one write of V) but
+// issues twice the LDS reads, which costs about 2% of a long kernel's time; the
+// host picks it where few query tiles share a key set (frame attention).  The
+// last (partial) tile of a key range is peeled out of the loop and its missing
+// keys are masked to -inf.
 //
 // Workgroup order is XCD-aware: the hardware deals workgroups round-robin to
 // the 8 XCDs, so the linear id is remapped to give each XCD a contiguous run
@@ -108,13 +118,16 @@ constexpr float kLow = -64.0f;
 constexpr float kLn2 = 0.693147180559945309f;
 
 typedef __attribute__((address_space(3))) void lds_void;
+// word 3 of a raw (untyped) buffer descriptor on gfx950: 32-bit data format, no swizzle
+constexpr int kBufferFlags = 0x00020000;
 
 // K tile:   row r holds key r of the tile, 8 units of 8 dims; unit u at slot u ^ row_swz(r).
-// V^T tile: row d holds channel d of the 64 keys; unit u holds operand keys 8(u%4)..+7 of
-//           32-key chunk u/4 (see the header for their key order), at slot u ^ col_swz(d).
+// V tile:   V^T tile: row d holds channel d of the 64 keys; unit u holds operand keys
+//           8(u%4)..+7 of 32-key chunk u/4 (see the header for their key order), at slot
+//           u ^ col_swz(d); or (V in place) a row tile laid out as the K tile.
 struct Smem {
   u32x4 k[NSTAGE][BK][8];
-  u32x4 vt[NSTAGE][D][8];
+  u32x4 v[NSTAGE][BK][8];
   int redo;  // some row of the optimistic pass is out of range: rerun the workgroup exactly
 };
 
@@ -162,6 +175,8 @@ __device__ __forceinline__ void static_for(F&& f) {
     __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);         \
   }
 
+// kVDirect: V rows are read in place from p.v, else V^T tiles from p.vt.
+template <bool kVDirect>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(VGGT_ATTN_WPE, VGGT_ATTN_WPE)))
 void attn_fwd_bf16_kernel(AttnProblem p) {
   __shared__ Smem sm;
@@ -209,6 +224,9 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
   const int64_t kseq = p.k_seq_stride != 0 ? seq : 0;
   const u32x4* __restrict__ ktg = (const u32x4*)p.k + (kseq * p.H + head) * p.ktiles_seq * 512;
   const u32x4* __restrict__ vtg = (const u32x4*)p.vt + (kseq * p.H + head) * p.ktiles_seq * 512;
+  // or V in place: key j of this sequence at vg + j * vrow bytes
+  const char* __restrict__ vg = (const char*)p.v + ((seq * p.k_seq_stride) * p.tok_stride + head * D) * 2;
+  const int vrow = (int)p.tok_stride * 2;  // at most 64 heads of 128 bytes
 
   const int kbeg = split * p.keys_per_split;
   const int kend = min(nk_seq, kbeg + p.keys_per_split);
@@ -217,17 +235,39 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
   const int q0 = qt * BQ + wave * QW;  // first query of this wave
   const bool active = q0 < nq_seq;
 
-  // ---- tile loads: each wave copies CPW 1 KiB blocks of the K tile and CPW of the V^T tile
+  // ---- tile loads: each wave copies CPW 1 KiB blocks (8 rows) of the K tile and CPW of the
+  //      V tile.  Lane l of a block fills slot l % 8 of its row l / 8; for V rows read in
+  //      place that slot holds unit (l % 8) ^ row_swz(row), and row_swz(row) = (l / 8) & 6
+  //      because blocks start at multiples of 8 rows.  A V block is a raw buffer load whose
+  //      descriptor (scalar registers) starts at the block's first key and ends after the
+  //      last key of the range: the lanes of rows past that end fall outside the descriptor,
+  //      and such a load writes zeros to LDS, so the padding rows hold zeros as in the K tiles.
   const int ktile0 = kbeg / BK;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int v_lane_off = (lane >> 3) * vrow + 16 * ((lane & 7) ^ ((lane >> 3) & 6));
   auto issue = [&](int stage, int tile) {
     // wave-uniform base (scalar registers) + the lane's 16-byte unit
     const u32x4* ks = ktg + (int64_t)(ktile0 + tile) * 512 + wave_u * (64 * CPW);
-    const u32x4* vs = vtg + (int64_t)(ktile0 + tile) * 512 + wave_u * (64 * CPW);
 #pragma unroll
-    for (int c = 0; c < CPW; ++c) {
+    for (int c = 0; c < CPW; ++c)
       __builtin_amdgcn_global_load_lds((const void*)(ks + 64 * c + lane), (lds_void*)&sm.k[stage][(CPW * wave_u + c) * 8][0], 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(vs + 64 * c + lane), (lds_void*)&sm.vt[stage][(CPW * wave_u + c) * 8][0], 16, 0, 0);
+    if constexpr (!kVDirect) {
+      const u32x4* vs = vtg + (int64_t)(ktile0 + tile) * 512 + wave_u * (64 * CPW);
+#pragma unroll
+      for (int c = 0; c < CPW; ++c)
+        __builtin_amdgcn_global_load_lds((const void*)(vs + 64 * c + lane), (lds_void*)&sm.v[stage][(CPW * wave_u + c) * 8][0], 16, 0, 0);
+    } else {
+      const int key0 = (ktile0 + tile) * BK + 8 * CPW * wave_u;  // first key of the wave's blocks
+#pragma unroll
+      for (int c = 0; c < CPW; ++c) {
+        const int kb = key0 + 8 * c;
+        // uniform by construction; readfirstlane keeps the descriptor in scalar registers
+        const int bytes = __builtin_amdgcn_readfirstlane(max(0, min(8, kend - kb)) * vrow);
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(vg + (int64_t)kb * vrow), 0, bytes, kBufferFlags);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)&sm.v[stage][(CPW * wave_u + c) * 8][0], 16,
+                                                 v_lane_off, 0, 0, 0);
+      }
     }
   };
 
@@ -342,15 +382,17 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
       }
     }
   };
-  auto read_v = [&](int stage) {
+  // 32-key chunk c of the V^T operand: 4 reads of the V^T tile or 8 transposing reads
+  auto read_v = [&](int stage, int c) {
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
+    for (int db = 0; db < 4; ++db) {
+      if constexpr (kVDirect) {
+        vf[c][db] = read_tr_rows(sm.v[stage], c, db, lane);
+      } else {
         const int d = 16 * db + l16;
-        const int u = 4 * c + g;
-        vf[c][db] = __builtin_bit_cast(bf16x8, sm.vt[stage][d][u ^ col_swz(d)]);
+        vf[c][db] = __builtin_bit_cast(bf16x8, sm.v[stage][d][(4 * c + g) ^ col_swz(d)]);
       }
+    }
   };
   // S^T of query block qb; the two products of a key block are four MFMAs apart
   auto qk = [&](f32x4 (&sd)[4], int qb) {
@@ -501,11 +543,16 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
       VGGT_INTERLEAVE8();
     }
     __builtin_amdgcn_sched_barrier(0);
-    // second half: S^T of the next step's block
-    if constexpr (b == 0) read_v(stage);
+    // second half: S^T of the next step's block; in step 0 also the tile's V fragments (the
+    // sixteen transposing reads split over both quarters)
+    if constexpr (b == 0) {
+      read_v(stage, 0);
+      if constexpr (!kVDirect) read_v(stage, 1);
+    }
     constexpr int nb = b < NQB - 1 ? b + 1 : 0;
     const bool has_next = b < NQB - 1 || !last;
     if constexpr (exact && first) {
+      if constexpr (b == 0 && kVDirect) read_v(stage, 1);
       if (has_next) qk(s[nxt], nb);
       slow(s[cur], b, true, pp[cur]);
     } else {
@@ -519,9 +566,14 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
         VGGT_INTERLEAVE4();
       }
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (b == 0 && kVDirect) read_v(stage, 1);
       if (has_next) qk_dc(s[nxt], nb, 1);
       soft_e(s[cur], 1, exact_c, mrow[b], pp[cur][1], 2, 4);
-      VGGT_INTERLEAVE4();
+      if constexpr (b == 0 && kVDirect) {
+        VGGT_INTERLEAVE4_DS2();
+      } else {
+        VGGT_INTERLEAVE4();
+      }
       if constexpr (exact) {
         if (__any(smax(s[cur]) - mrow[b] > kRaise)) slow(s[cur], b, false, pp[cur]);
       }
@@ -637,7 +689,10 @@ hipError_t launch_attn_bf16(const AttnProblem& p, hipStream_t stream) {
   const int ntq = (p.nq + BQ - 1) / BQ;
   const int64_t nwg = (int64_t)ntq * p.H * p.nseq * p.splits;
   if (nwg <= 0) return hipSuccess;
-  hipLaunchKernelGGL(attn_fwd_bf16_kernel, dim3((unsigned)nwg), dim3(NT), 0, stream, p);
+  if (p.vt)
+    hipLaunchKernelGGL(attn_fwd_bf16_kernel<false>, dim3((unsigned)nwg), dim3(NT), 0, stream, p);
+  else
+    hipLaunchKernelGGL(attn_fwd_bf16_kernel<true>, dim3((unsigned)nwg), dim3(NT), 0, stream, p);
   return hipGetLastError();
 }
 

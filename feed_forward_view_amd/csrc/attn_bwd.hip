@@ -59,29 +59,6 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 w) { return __builtin_bit_cast(bf16x8, w); }
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-// The A operand of a 16x16x32 product whose M dimension is the 64 channels of a row tile
-// (rows are keys or queries, 8 x 16-byte units per row, unit u at slot u ^ row_swz(row)):
-// channel block db (16 channels) of 32-row chunk c, the chunk's rows in operand order (lane l
-// holds channel 16db + l%16 of rows 4(l/16) + 0..3 and 16 + 4(l/16) + 0..3).  Two transposing
-// LDS reads: within each 16-lane group, lane 4r + q reads the 8 bytes of channels
-// 16db + 4q .. +3 of one row, and lane j of the group receives element j % 4 of lane
-// 4r' + j / 4's bytes as its element r', i.e. channel 16db + j of the four rows the group read.
-__device__ __forceinline__ bf16x8 read_tr_a(const u32x4 (&tile)[64][8], int c, int db, int lane) {
-  const int g = lane >> 4, r = (lane >> 2) & 3, q = lane & 3;
-  const int u = 2 * db + (q >> 1);
-  u32x2 half[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int row = 32 * c + 16 * h + 4 * g + r;
-    const char* src = (const char*)&tile[row][u ^ row_swz(row)] + 8 * (q & 1);
-    half[h] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)src));
-  }
-  return as_bf16x8(u32x4{half[0][0], half[0][1], half[1][0], half[1][1]});
-}
-
 // Workgroup barrier for the tile ring.  __syncthreads() would make the compiler drain every
 // outstanding copy first, including the next tile's, which was issued just before; the
 // explicit counter waits already cover the copies each barrier needs.  The empty asm keeps
@@ -216,7 +193,7 @@ void attn_bwd_dq_kernel(AttnBwdProblem p) {
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int db = 0; db < 4; ++db) ktf[c][db] = read_tr_a(sm.k[stage], c, db, lane);
+      for (int db = 0; db < 4; ++db) ktf[c][db] = read_tr_rows(sm.k[stage], c, db, lane);
     const bool tail = t == p.ntile - 1 && 64 * p.ntile > p.n;
     // S^T and dP^T of a query block (lane holds keys 16kb + 4g + r of its query), and
     // dS^T = P dP^T as the bf16 B operand of dQ^T += K^T dS^T for 32-key chunk c.  The tile is
@@ -413,8 +390,8 @@ void attn_bwd_dkdv_kernel(AttnBwdProblem p) {
       bf16x8 dtf[4], qtf[4];
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        dtf[db] = read_tr_a(sm.d[stage], c, db, lane);
-        qtf[db] = read_tr_a(sm.q[stage], c, db, lane);
+        dtf[db] = read_tr_rows(sm.d[stage], c, db, lane);
+        qtf[db] = read_tr_rows(sm.q[stage], c, db, lane);
       }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {

@@ -267,12 +267,24 @@ vggt_status validate_attn(const QKVO& t, const int32_t* pos, float base, size_t 
 
 int64_t pad64(int64_t n) { return (n + 63) / 64 * 64; }
 
-// Workspace layout of one attention call.  bf16: RoPE table, rotated K and
-// transposed V for the matrix-core kernel; fp32: rotated copies of Q and K.
-// Both: split partials.  Offsets are 256-byte aligned.
+// The bf16 kernel reads V rows in place (no V^T pre-pass) when fewer than this many query
+// tiles share a key set.  The pre-pass costs one read and one write of V; reading in place
+// costs twice the LDS reads of the V operand in every query tile, about 2% of the kernel's
+// time (measured at 6 query tiles per key set, frame attention at T = 1374, where reading in
+// place saves 4% of the call, and at 172, global attention at N = 43968, where it costs 1.5%).
+constexpr int kVInPlaceMaxQueryTiles = 32;
+bool v_in_place(int64_t nq) {
+  const int bq = vggt::attn_bf16_query_tile();
+  return (nq + bq - 1) / bq < kVInPlaceMaxQueryTiles;
+}
+
+// Workspace layout of one attention call.  bf16: RoPE table, rotated K and,
+// unless V is read in place, transposed V for the matrix-core kernel; fp32:
+// rotated copies of Q and K.  Both: split partials.  Offsets are 256-byte
+// aligned.
 struct Layout {
   size_t table = 0, qr = 0, kr = 0, kt = 0, vt = 0, part_o = 0, part_ml = 0, total = 0;
-  bool use_table = false, use_qr = false, use_kr = false;
+  bool use_table = false, use_qr = false, use_kr = false, use_vt = false;
   int ktiles = 0;  // bf16: key tiles of 64 per sequence
   SplitPlan sp{1, 0};
 };
@@ -284,8 +296,9 @@ void add(Layout& L, size_t& off, size_t bytes) {
 
 // nseq sequences of nq queries and nk keys; q tensor has nseq*nq tokens,
 // k/v tensors nseq*nk tokens; positions repeat every rope_T tokens.
-// bf16: RoPE table plus K and V^T in 64-key tile layout; fp32: rotated copies
-// of Q and K.  Both: split partials.  Offsets are 256-byte aligned.
+// bf16: RoPE table plus K and (unless V is read in place) V^T in 64-key tile
+// layout; fp32: rotated copies of Q and K.  Both: split partials.  Offsets are
+// 256-byte aligned.
 Layout plan(int nseq, int64_t nq, int64_t nk, int H, int rope_T, bool rope_on, bool allow_split, int kv_splits,
             vggt_dtype dt, bool norm_on = false) {
   Layout L;
@@ -298,7 +311,8 @@ Layout plan(int nseq, int64_t nq, int64_t nk, int H, int rope_T, bool rope_on, b
     L.ktiles = (int)((nk + 63) / 64);
     const size_t tiles_bytes = (size_t)nseq * H * L.ktiles * 64 * vggt::kHeadDim * 2;
     add(L, L.kt, tiles_bytes);
-    add(L, L.vt, tiles_bytes);
+    L.use_vt = !v_in_place(nq);
+    if (L.use_vt) add(L, L.vt, tiles_bytes);
   } else if (rope_on || norm_on) {
     L.use_qr = true;
     add(L, L.qr, (size_t)nseq * nq * H * vggt::kHeadDim * es);
@@ -347,12 +361,12 @@ hipError_t run_call(const Layout& L, vggt::AttnProblem p, vggt_dtype dt, int nse
                                   table, rope_T,
                                   norm ? norm->k_gamma : nullptr, norm ? norm->k_beta : nullptr,
                                   norm ? norm->eps : 0.0f, st);
-    if (e == hipSuccess)
+    if (e == hipSuccess && L.use_vt)
       e = vggt::launch_v_tiles_bf16(vggt::contiguous_keys(p.v, (int)nk), ws + L.vt, nseq, (int)nk, H,
                                     st);
     if (e != hipSuccess) return e;
     p.k = ws + L.kt;
-    p.vt = ws + L.vt;
+    p.vt = L.use_vt ? ws + L.vt : nullptr;
     p.ktiles_seq = L.ktiles;
   } else if (L.use_qr) {
     // fp32: LayerNorm and/or RoPE into the rotated copies
@@ -869,13 +883,14 @@ namespace {
 constexpr int kMaxExtra = 4096;
 
 // Workspace of one frame/global "ex" call.  bf16: RoPE table and the key
-// tiles of the compacted key set; fp32: normalised/rotated copies and the
-// gathered key set.  Global calls also hold the split partials of the frame
-// tokens' queries and of the extra tokens' queries.
+// tiles of the compacted key set (V^T tiles unless a frame's V rows are read
+// in place); fp32: normalised/rotated copies and the gathered key set.  Global
+// calls also hold the split partials of the frame tokens' queries and of the
+// extra tokens' queries.
 struct ExLayout {
   size_t table = 0, kt = 0, vt = 0, qr = 0, kc = 0, vc = 0, xqr = 0;
   size_t part_o = 0, part_ml = 0, xpart_o = 0, xpart_ml = 0, total = 0;
-  bool use_qr = false, use_kc = false, use_vc = false, use_xqr = false;
+  bool use_qr = false, use_kc = false, use_vc = false, use_xqr = false, use_vt = false;
   int nseq_k = 1;
   int64_t nk = 0;
   int ktiles = 0;
@@ -898,7 +913,10 @@ ExLayout plan_ex(bool global, int S, int T, int Ta, int E, int H, int kv_splits,
     L.ktiles = (int)((L.nk + 63) / 64);
     const size_t tiles = (size_t)L.nseq_k * H * L.ktiles * 64 * vggt::kHeadDim * 2;
     add_ex(L, L.kt, tiles);
-    add_ex(L, L.vt, tiles);
+    // a frame's active tokens are a contiguous run of V rows; the global key set (active
+    // tokens of every frame, then the extras) is not, and always goes through V^T tiles
+    L.use_vt = global || !v_in_place(Ta);
+    if (L.use_vt) add_ex(L, L.vt, tiles);
   } else {
     if (rope || norm) {
       L.use_qr = true;
@@ -984,10 +1002,10 @@ hipError_t run_ex(const ExLayout& L, const ExArgs& a, vggt_dtype dt, char* ws, h
     e = vggt::launch_k_tiles_bf16(ks, ws + L.kt, L.nseq_k, (int)L.nk, H, table, a.T,
                                   a.norm ? a.norm->k_gamma : nullptr, a.norm ? a.norm->k_beta : nullptr,
                                   a.norm ? a.norm->eps : 0.0f, st);
-    if (e == hipSuccess) e = vggt::launch_v_tiles_bf16(vs, ws + L.vt, L.nseq_k, (int)L.nk, H, st);
+    if (e == hipSuccess && L.use_vt) e = vggt::launch_v_tiles_bf16(vs, ws + L.vt, L.nseq_k, (int)L.nk, H, st);
     if (e != hipSuccess) return e;
     p.k = ws + L.kt;
-    p.vt = ws + L.vt;
+    p.vt = L.use_vt ? ws + L.vt : nullptr;
     p.ktiles_seq = L.ktiles;
   } else {
     const int64_t full = (int64_t)a.S * a.T;
@@ -1032,7 +1050,7 @@ hipError_t run_ex(const ExLayout& L, const ExArgs& a, vggt_dtype dt, char* ws, h
   p.q_seq_stride = a.T;
   p.nq_total = (int64_t)a.S * a.Ta;
   p.nk = (int)L.nk;
-  p.k_seq_stride = a.global ? 0 : (dt == VGGT_BF16 ? L.nk : a.T);
+  p.k_seq_stride = a.global ? 0 : a.T;  // tokens between frames (bf16: nonzero = per-frame tiles)
   p.splits = L.sp.splits;
   p.keys_per_split = L.sp.keys_per_split;
   if (L.sp.splits > 1) {

@@ -36,14 +36,38 @@ __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w 
 // ds_read_b64_tr_b16 in two passes of 32 lanes (the two half-waves); both lane groupings
 // were measured with a bank-conflict counter.  The operand reads are
 //   * ds_read_b128: lane l reads unit 4c + l/16 of row base + l % 16;
-//   * ds_read_b64_tr_b16 (gradient kernels): the lanes of a half-wave read 32 bytes (units
-//     2db, 2db + 1) of each of 8 consecutive rows.
+//   * ds_read_b64_tr_b16 (gradient kernels, and the forward kernel's V operand when it reads
+//     V rows in place): the lanes of a half-wave read 32 bytes (units 2db, 2db + 1) of each
+//     of 8 consecutive rows.
 // row_swz = r & 6 makes both conflict-free: in a b128 pass the four blocks cover rows
 // {4i..4i+3} of two units of opposite parity, and (r & 1, u ^ (r & 6)) differs for all 16
 // lanes; in a transposing half-wave, (r & 1, (r >> 1) & 3) differs for all 8 rows.  col_swz
 // serves only b128 reads.
 __device__ __forceinline__ int row_swz(int r) { return r & 6; }
 __device__ __forceinline__ int col_swz(int d) { return (d >> 1) & 7; }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// The A operand of a 16x16x32 product whose M dimension is the 64 channels of a row tile
+// (rows are keys or queries, 8 x 16-byte units per row, unit u at slot u ^ row_swz(row)):
+// channel block db (16 channels) of 32-row chunk c, the chunk's rows in operand order (lane l
+// holds channel 16db + l%16 of rows 4(l/16) + 0..3 and 16 + 4(l/16) + 0..3).  Two transposing
+// LDS reads: within each 16-lane group, lane 4r + q reads the 8 bytes of channels
+// 16db + 4q .. +3 of one row, and lane j of the group receives element j % 4 of lane
+// 4r' + j / 4's bytes as its element r', i.e. channel 16db + j of the four rows the group read.
+__device__ __forceinline__ bf16x8 read_tr_rows(const u32x4 (&tile)[64][8], int c, int db, int lane) {
+  const int g = lane >> 4, r = (lane >> 2) & 3, q = lane & 3;
+  const int u = 2 * db + (q >> 1);
+  u32x2 half[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int row = 32 * c + 16 * h + 4 * g + r;
+    const char* src = (const char*)&tile[row][u ^ row_swz(row)] + 8 * (q & 1);
+    half[h] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)src));
+  }
+  return __builtin_bit_cast(bf16x8, u32x4{half[0][0], half[0][1], half[1][0], half[1][1]});
+}
 
 // Workgroups are dealt round-robin to the 8 XCDs; this maps the hardware id w
 // of nwg workgroups to a logical id such that each XCD receives a contiguous
@@ -63,8 +87,9 @@ __device__ __forceinline__ void xcd_remap(int w, int nwg, int& logical) {
 struct AttnProblem {
   const void* q;
   const void* k;
-  const void* v;           // V [tokens][H][64] (fp32 kernel)
-  const void* vt;          // bf16 kernel: V^T tiles [nseq][H][ntile][64][64]; K is in p.k as K tiles
+  const void* v;           // V [tokens][H][64]: fp32 kernel, and bf16 kernel when vt is null
+  const void* vt;          // bf16 kernel: V^T tiles [nseq][H][ntile][64][64], or null (V rows
+                           // are then read from v in place); K is in p.k as K tiles
   int ktiles_seq;          // bf16 kernel: key tiles per sequence in the tile layouts
   const f32x2* rope_tab;   // [rope_T][32] (cos, sin) applied to Q in the bf16 kernel, or null
   int rope_T;              // token positions repeat every rope_T tokens

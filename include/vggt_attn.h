@@ -159,8 +159,9 @@ vggt_status vggt_frame_attn(const void* q, const void* k, const void* v, void* o
  * process ends.  The call itself allocates, frees and synchronises nothing.
  *   Limit: vggt_frame_attn_workspace(S, T, H, pos_yx != NULL, dt) must not
  *   exceed VGGT_NOALLOC_SCRATCH_BYTES, else VGGT_ERR_WORKSPACE before anything
- *   is enqueued (bf16 with RoPE: S * H * ceil(T / 64) <= about 4000, e.g. 8
- *   frames of 1374 tokens x 16 heads).
+ *   is enqueued (bf16 with RoPE: S * H * ceil(T / 64) <= about 8000 for
+ *   frames under 8192 tokens, e.g. 22 frames of 1374 tokens x 16 heads; about
+ *   4000 for longer frames, whose V also goes through a tile pre-pass).
  *   Every call on one device uses the same array: calls that may overlap on
  *   one device (different streams without ordering) race; order them.
  */

@@ -58,8 +58,10 @@ def test_workspace_queries(L):
     BF16, F32 = 0, 1
     S, T, H = 4, 261, 16
     tensor = S * T * H * 64
-    # bf16: K and V^T in 64-key tiles (keys padded to 64 per sequence); with RoPE also the cos/sin table
-    tiles = 2 * S * H * 5 * 64 * 64 * 2
+    # bf16: K in 64-key tiles (keys padded to 64 per sequence), and V^T tiles too when 32 or
+    # more 256-query tiles share a key set (else V is read in place); with RoPE also the
+    # cos/sin table
+    tiles = S * H * 5 * 64 * 64 * 2
     assert L.vggt_frame_attn_workspace(S, T, H, 0, BF16) == tiles
     assert L.vggt_frame_attn_workspace(S, T, H, 1, BF16) >= tiles + T * 32 * 8
     # fp32 debug: nothing without RoPE, rotated Q and K copies with it
@@ -68,7 +70,10 @@ def test_workspace_queries(L):
     # explicit splits add the fp32 partials (64 values + max + sum per row and head)
     n = S * T
     base = L.vggt_global_attn_workspace(S, T, H, 1, 0, BF16)
-    assert base >= 2 * H * 17 * 64 * 64 * 2
+    assert base == H * 17 * 64 * 64 * 2  # 5 query tiles: V in place
+    big = (32 * 256 + 63) // 64  # 32 query tiles of one sequence: K and V^T tiles
+    assert L.vggt_global_attn_workspace(1, 32 * 256, H, 1, 0, BF16) == 2 * H * big * 64 * 64 * 2
+    assert L.vggt_global_attn_workspace(1, 31 * 256, H, 1, 0, BF16) == H * (31 * 4) * 64 * 64 * 2
     assert L.vggt_global_attn_workspace(S, T, H, 3, 0, BF16) >= base + 3 * n * H * (64 + 2) * 4
     assert L.vggt_global_attn_workspace(S, T, H, 1, 0, F32) == 0
     assert L.vggt_descriptor_xattn_workspace(100, 1374, 366, 16, 1, F32) == 0
@@ -206,8 +211,9 @@ def test_qk_norm_arguments(L):
 def test_omega_variant_arguments(L):
     BF16, F32 = 0, 1
     S, T, Ta, E, H = 4, 1040, 1024, 5, 16
-    # bf16: tiles of the compacted key set (frame: per frame; global: active tokens plus extras)
-    assert L.vggt_frame_attn_ex_workspace(S, T, Ta, H, 0, BF16) == 2 * S * H * 16 * 64 * 64 * 2
+    # bf16: K tiles of the compacted key set (frame: per frame, V read in place; global: active
+    # tokens plus extras, with V^T tiles)
+    assert L.vggt_frame_attn_ex_workspace(S, T, Ta, H, 0, BF16) == S * H * 16 * 64 * 64 * 2
     ws = L.vggt_global_attn_ex_workspace(S, T, Ta, E, H, 1, 0, BF16)
     assert ws >= 2 * H * ((S * Ta + E + 63) // 64) * 64 * 64 * 2
     assert L.vggt_global_attn_ex_workspace(S, T, T + 1, E, H, 1, 0, BF16) == 0

@@ -74,15 +74,19 @@ def test_omega_variants_small(dtype, rope, norm):
         assert bool((go[:, Ta:] == SENTINEL).all()), "register rows of the output were written"
 
 
-def test_global_ex_without_extras_matches_global():
-    wl = workload.Workload("t", 52, S=2, gh=8, gw=8, n_special=5, patch_begin=5, H=2)
+@pytest.mark.parametrize("splits", [1, 3])
+def test_global_ex_without_extras_matches_global(splits):
+    # N = 3 * 149 = 447 keys: 7 key tiles, the last holding 63 keys
+    wl = workload.Workload("t", 52, S=3, gh=12, gw=12, n_special=5, patch_begin=5, H=2)
     q, k, v = wl.qkv_bf16()
     pd = torch.from_numpy(wl.positions()).to(dev())
     qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
-    a, x = ffv.vggt_global_attn_ex(qd, kd, vd, wl.T, pos_yx=pd, kv_splits=1)
+    a, x = ffv.vggt_global_attn_ex(qd, kd, vd, wl.T, pos_yx=pd, kv_splits=splits)
     assert x is None
-    b = ffv.vggt_global_attn(qd, kd, vd, pos_yx=pd, kv_splits=1)
-    # same keys, key tiles and arithmetic per query; only the query-tile grouping differs
+    b = ffv.vggt_global_attn(qd, kd, vd, pos_yx=pd, kv_splits=splits)
+    # same keys, key tiles and arithmetic per query; the query-tile grouping differs, and the
+    # V operand comes from V^T tiles (compacted key set) in one call and from V rows read in
+    # place (two query tiles) in the other
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16)), \
         f"max diff {(a.float() - b.float()).abs().max().item():.3e}"

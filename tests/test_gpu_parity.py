@@ -150,6 +150,23 @@ def test_ragged_shapes(T, H):
             check_bf16(go, ref, f"global T={T} H={H} rope={use_pos} splits={splits}")
 
 
+@pytest.mark.parametrize("T", [69, 128])
+def test_frame_v_rows_stay_inside_the_frame(T):
+    # Frame attention reads V rows in place; the last key tile of frame 0 covers rows of
+    # frame 1 (T = 69: 59 of its 64 rows).  With frame 1's V all NaN, frames 0 and 2 must
+    # still match the oracle: rows past a frame's keys are never read into the P V product.
+    S, H = 3, 2
+    q = workload.normal_bf16(0xF0, (S, T, H, 64))
+    k = workload.normal_bf16(0xF1, (S, T, H, 64))
+    v = workload.normal_bf16(0xF2, (S, T, H, 64))
+    v[1] = 0x7FC0  # bf16 quiet NaN
+    out = to_f64(ffv.vggt_frame_attn(to_dev(q), to_dev(k), to_dev(v)))
+    for s in (0, 2):
+        ref = oracle.frame_attn(q[s:s + 1], k[s:s + 1], v[s:s + 1], 1, T)
+        check_bf16(out[s:s + 1], ref, f"frame {s} beside a NaN frame, T={T}")
+    assert np.isnan(out[1]).all()
+
+
 def test_single_token_frames_return_values():
     q = workload.normal_bf16(5, (4, 1, 2, 64))
     v = workload.normal_bf16(6, (4, 1, 2, 64))
