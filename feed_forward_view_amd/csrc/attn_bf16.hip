@@ -271,81 +271,110 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
     }
   };
 
+  // ---- Q fragments (B operand of S^T = K Q^T): lane holds query q0 + 16qb + l16,
+  //      channels 32dc + 8g .. +7 (the other 48 sit in the lanes of the same l16),
+  //      after an optional per-head LayerNorm, rotated and scaled by scale*log2(e).
+  //      Every global operand of this prologue (Q words, cos/sin pairs, LayerNorm
+  //      parameters) is loaded before the first tile copies are issued: loads complete in
+  //      issue order, so the wait for them then leaves the copies in flight, and the tile
+  //      latency overlaps the prologue's arithmetic instead of adding to it.
+  const f32x2* __restrict__ tab = p.rope_tab;
+  u32x4 qw[NQB][2];  // raw bf16 words [qb][dc]
+  f32x4 cs[NQB][2][2];  // (cos, sin) of rotation pairs 16dc + 4g + 2h + 0, 1 [qb][dc][h]
+  float lng[2][4][2], lnb[2][4][2];  // LayerNorm gamma / beta of channels 32dc + 8g + 2e + 0, 1
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    const int qi = q0 + 16 * qb + l16;
+    const bool ok = qi < nq_seq;
+    const int qrow = ok ? qi : 0;
+#pragma unroll
+    for (int dc = 0; dc < 2; ++dc) {
+      qw[qb][dc] = *(const u32x4*)(qg + (int64_t)qrow * p.tok_stride + 32 * dc + 8 * g);
+      if (!ok) qw[qb][dc] = u32x4{0u, 0u, 0u, 0u};
+    }
+    if (tab) {
+      const int tpos = (int)((seq * p.q_seq_stride + qrow) % p.rope_T);
+      const f32x4* trow = (const f32x4*)(tab + tpos * 32);
+#pragma unroll
+      for (int dc = 0; dc < 2; ++dc)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) cs[qb][dc][h] = trow[8 * dc + 2 * g + h];
+    }
+  }
+  if (p.q_ln_g) {
+#pragma unroll
+    for (int dc = 0; dc < 2; ++dc)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int c = 32 * dc + 8 * g + 2 * e;  // the parameters need only 4-byte alignment
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          lng[dc][e][j] = p.q_ln_g[c + j];
+          lnb[dc][e][j] = p.q_ln_b[c + j];
+        }
+      }
+  }
+
 #pragma unroll
   for (int i = 0; i < NSTAGE - 1; ++i)
     if (i < ntiles) issue(i, i);
 
-  // ---- Q fragments (B operand of S^T = K Q^T): lane holds query q0 + 16qb + l16,
-  //      channels 32dc + 8g .. +7 (the other 48 sit in the lanes of the same l16),
-  //      after an optional per-head LayerNorm, rotated and scaled by scale*log2(e).
   bf16x8 qf[NQB][2];
-  {
-    const f32x2* __restrict__ tab = p.rope_tab;
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      const int qi = q0 + 16 * qb + l16;
-      const bool ok = qi < nq_seq;
-      const int qrow = ok ? qi : 0;
-      const int tpos = tab ? (int)((seq * p.q_seq_stride + qrow) % p.rope_T) : 0;
-      const f32x2* trow = tab ? tab + tpos * 32 : nullptr;
-      float x[2][4], y[2][4];  // [dc][pair]: channels 32dc + 8g + 2e, +1
+  for (int qb = 0; qb < NQB; ++qb) {
+    float x[2][4], y[2][4];  // [dc][pair]: channels 32dc + 8g + 2e, +1
 #pragma unroll
-      for (int dc = 0; dc < 2; ++dc) {
-        u32x4 w = *(const u32x4*)(qg + (int64_t)qrow * p.tok_stride + 32 * dc + 8 * g);
-        if (!ok) w = u32x4{0u, 0u, 0u, 0u};
+    for (int dc = 0; dc < 2; ++dc)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[dc][e] = lo_bf16(qw[qb][dc][e]);
+        y[dc][e] = hi_bf16(qw[qb][dc][e]);
+      }
+    if (p.q_ln_g) {
+      float sum = 0.0f;
+#pragma unroll
+      for (int dc = 0; dc < 2; ++dc)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sum += x[dc][e] + y[dc][e];
+      sum += __shfl_xor(sum, 16);
+      sum += __shfl_xor(sum, 32);
+      const float mu = sum * (1.0f / D);
+      float dev = 0.0f;
+#pragma unroll
+      for (int dc = 0; dc < 2; ++dc)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          x[dc][e] = lo_bf16(w[e]);
-          y[dc][e] = hi_bf16(w[e]);
+          dev = __builtin_fmaf(x[dc][e] - mu, x[dc][e] - mu, dev);
+          dev = __builtin_fmaf(y[dc][e] - mu, y[dc][e] - mu, dev);
+        }
+      dev += __shfl_xor(dev, 16);
+      dev += __shfl_xor(dev, 32);
+      const float inv = 1.0f / __builtin_sqrtf(dev * (1.0f / D) + p.ln_eps);
+#pragma unroll
+      for (int dc = 0; dc < 2; ++dc)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[dc][e] = __builtin_fmaf((x[dc][e] - mu) * inv, lng[dc][e][0], lnb[dc][e][0]);
+          y[dc][e] = __builtin_fmaf((y[dc][e] - mu) * inv, lng[dc][e][1], lnb[dc][e][1]);
+        }
+    }
+#pragma unroll
+    for (int dc = 0; dc < 2; ++dc) {
+      if (tab) {
+        // rotation pairs 16dc + 4g + e of the 32 of this position
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float c = cs[qb][dc][e >> 1][2 * (e & 1)], sn = cs[qb][dc][e >> 1][2 * (e & 1) + 1];
+          const float x2 = __builtin_fmaf(x[dc][e], c, -y[dc][e] * sn);
+          const float y2 = __builtin_fmaf(x[dc][e], sn, y[dc][e] * c);
+          x[dc][e] = x2;
+          y[dc][e] = y2;
         }
       }
-      if (p.q_ln_g) {
-        float sum = 0.0f;
+      u32x4 r;
 #pragma unroll
-        for (int dc = 0; dc < 2; ++dc)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) sum += x[dc][e] + y[dc][e];
-        sum += __shfl_xor(sum, 16);
-        sum += __shfl_xor(sum, 32);
-        const float mu = sum * (1.0f / D);
-        float dev = 0.0f;
-#pragma unroll
-        for (int dc = 0; dc < 2; ++dc)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            dev = __builtin_fmaf(x[dc][e] - mu, x[dc][e] - mu, dev);
-            dev = __builtin_fmaf(y[dc][e] - mu, y[dc][e] - mu, dev);
-          }
-        dev += __shfl_xor(dev, 16);
-        dev += __shfl_xor(dev, 32);
-        const float inv = 1.0f / __builtin_sqrtf(dev * (1.0f / D) + p.ln_eps);
-#pragma unroll
-        for (int dc = 0; dc < 2; ++dc)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int c = 32 * dc + 8 * g + 2 * e;
-            x[dc][e] = __builtin_fmaf((x[dc][e] - mu) * inv, p.q_ln_g[c], p.q_ln_b[c]);
-            y[dc][e] = __builtin_fmaf((y[dc][e] - mu) * inv, p.q_ln_g[c + 1], p.q_ln_b[c + 1]);
-          }
-      }
-#pragma unroll
-      for (int dc = 0; dc < 2; ++dc) {
-        if (trow) {
-          // rotation pairs 16dc + 4g + e of the 32 of this position
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const f32x2 cs = trow[16 * dc + 4 * g + e];
-            const float x2 = __builtin_fmaf(x[dc][e], cs[0], -y[dc][e] * cs[1]);
-            const float y2 = __builtin_fmaf(x[dc][e], cs[1], y[dc][e] * cs[0]);
-            x[dc][e] = x2;
-            y[dc][e] = y2;
-          }
-        }
-        u32x4 r;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) r[e] = pack_bf16x2(x[dc][e] * p.scale_log2, y[dc][e] * p.scale_log2);
-        qf[qb][dc] = __builtin_bit_cast(bf16x8, r);
-      }
+      for (int e = 0; e < 4; ++e) r[e] = pack_bf16x2(x[dc][e] * p.scale_log2, y[dc][e] * p.scale_log2);
+      qf[qb][dc] = __builtin_bit_cast(bf16x8, r);
     }
   }
 
