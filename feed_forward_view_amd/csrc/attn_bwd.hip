@@ -253,6 +253,10 @@ void attn_bwd_dq_kernel(AttnBwdProblem p) {
       __builtin_amdgcn_sched_group_barrier(0x400, 1, 0);  // exponential
       __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);  // other VALU
     }
+    // the phase's weights are complete here: without this use the compiler sinks their
+    // exponentials and packs past the phase boundary, next to their first use in the next
+    // phase, and the hints above find no VALU work to place beside the MFMAs
+    asm volatile("" ::"v"(w0[0]), "v"(w0[1]));
     __builtin_amdgcn_sched_barrier(0);
     mask(1);
     dq(0, w0);
@@ -264,6 +268,7 @@ void attn_bwd_dq_kernel(AttnBwdProblem p) {
       __builtin_amdgcn_sched_group_barrier(0x400, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
     }
+    asm volatile("" ::"v"(w1[0]), "v"(w1[1]));
     __builtin_amdgcn_sched_barrier(0);
     dq(1, w1);
   }
@@ -360,56 +365,107 @@ void attn_bwd_dkdv_kernel(AttnBwdProblem p) {
       wait_vmcnt<0>();
     }
     tile_barrier();  // ... in every wave's copies
-    // the tile's 64 queries as two 32-query chunks c, each two 16-query blocks
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      f32x4 s[2][2], dp[2][2];  // [block 2c + i][kb]: queries 16(2c+i) + 4g + r, the lane's key
+    // The tile's 64 queries are two 32-query chunks c, each two 16-query blocks.  Four
+    // phases, so that each chunk's exponentials, products and packs run beside the other
+    // chunk's independent MFMAs:  S,dP(0) | S,dP(1) + P,dS(0) | dV,dK(0) + P,dS(1) | dV,dK(1).
+    // Each phase reads the LDS operands of the next one.
+    struct RowOps {
+      bf16x8 qr[2][2], dr[2][2];  // [block i][dc]: Q and dO rows of the chunk's blocks
+      f32x4 nl[2], nd[2];         // -lse2 and -D of the register's queries
+    };
+    auto read_rows = [&](int c, RowOps& r) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int qb = 2 * c + i, row = 16 * qb + l16;
-        // accumulator inputs: -lse2 and -D of the register's queries 16qb + 4g + r
-        const f32x4 nl = *(const f32x4*)&sm.st[stage][0][16 * qb + 4 * g];
-        const f32x4 nd = *(const f32x4*)&sm.st[stage][1][16 * qb + 4 * g];
-        bf16x8 qr[2], dr[2];
+        r.nl[i] = *(const f32x4*)&sm.st[stage][0][16 * qb + 4 * g];
+        r.nd[i] = *(const f32x4*)&sm.st[stage][1][16 * qb + 4 * g];
 #pragma unroll
         for (int dc = 0; dc < 2; ++dc) {
           const int slot = (4 * dc + g) ^ row_swz(row);
-          qr[dc] = as_bf16x8(sm.q[stage][row][slot]);
-          dr[dc] = as_bf16x8(sm.d[stage][row][slot]);
-        }
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          s[i][kb] = mfma16(qr[0], kf[kb][0], nl);
-          s[i][kb] = mfma16(qr[1], kf[kb][1], s[i][kb]);
-          dp[i][kb] = mfma16(dr[0], vf[kb][0], nd);
-          dp[i][kb] = mfma16(dr[1], vf[kb][1], dp[i][kb]);
+          r.qr[i][dc] = as_bf16x8(sm.q[stage][row][slot]);
+          r.dr[i][dc] = as_bf16x8(sm.d[stage][row][slot]);
         }
       }
-      // P and dS = P dP as the bf16 B operands (queries of chunk c in operand order) of
-      // dV^T += dO^T P and dK^T += Q^T dS
-      bf16x8 dtf[4], qtf[4];
+    };
+    // dO^T and Q^T of chunk c: the A operands of dV^T += dO^T P and dK^T += Q^T dS
+    auto read_tr = [&](int c, bf16x8 (&dtf)[4], bf16x8 (&qtf)[4]) {
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         dtf[db] = read_tr_rows(sm.d[stage], c, db, lane);
         qtf[db] = read_tr_rows(sm.q[stage], c, db, lane);
       }
+    };
+    // S and dP of the chunk's blocks: [block i][kb], queries 16(2c+i) + 4g + r, the lane's key
+    auto sdp = [&](const RowOps& r, f32x4 (&sc)[2][2], f32x4 (&dpc)[2][2]) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        u32x4 pw, sw;
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          sc[i][kb] = mfma16(r.qr[i][0], kf[kb][0], r.nl[i]);
+          dpc[i][kb] = mfma16(r.dr[i][0], vf[kb][0], r.nd[i]);
+        }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          sc[i][kb] = mfma16(r.qr[i][1], kf[kb][1], sc[i][kb]);
+          dpc[i][kb] = mfma16(r.dr[i][1], vf[kb][1], dpc[i][kb]);
+        }
+    };
+    // P and dS = P dP as the bf16 B operands (the chunk's queries in operand order)
+    auto pds = [&](const f32x4 (&sc)[2][2], const f32x4 (&dpc)[2][2], u32x4 (&pw)[2], u32x4 (&sw)[2]) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = e >> 1, r = 2 * (e & 1);
-          const float p0 = __builtin_amdgcn_exp2f(s[i][kb][r]), p1 = __builtin_amdgcn_exp2f(s[i][kb][r + 1]);
-          pw[e] = pack_bf16x2(p0, p1);
-          sw[e] = pack_bf16x2(p0 * dp[i][kb][r], p1 * dp[i][kb][r + 1]);
+          const float p0 = __builtin_amdgcn_exp2f(sc[i][kb][r]), p1 = __builtin_amdgcn_exp2f(sc[i][kb][r + 1]);
+          pw[kb][e] = pack_bf16x2(p0, p1);
+          sw[kb][e] = pack_bf16x2(p0 * dpc[i][kb][r], p1 * dpc[i][kb][r + 1]);
         }
+    };
+    auto dvdk = [&](const bf16x8 (&dtf)[4], const bf16x8 (&qtf)[4], const u32x4 (&pw)[2], const u32x4 (&sw)[2]) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
-          dva[kb][db] = mfma16(dtf[db], as_bf16x8(pw), dva[kb][db]);
-          dka[kb][db] = mfma16(qtf[db], as_bf16x8(sw), dka[kb][db]);
+          dva[kb][db] = mfma16(dtf[db], as_bf16x8(pw[kb]), dva[kb][db]);
+          dka[kb][db] = mfma16(qtf[db], as_bf16x8(sw[kb]), dka[kb][db]);
         }
-      }
+    };
+    RowOps r0, r1;
+    f32x4 s0[2][2], dp0[2][2], s1[2][2], dp1[2][2];
+    bf16x8 dtf0[4], qtf0[4], dtf1[4], qtf1[4];
+    u32x4 pw0[2], sw0[2], pw1[2], sw1[2];
+    read_rows(0, r0);
+    sdp(r0, s0, dp0);
+    read_rows(1, r1);
+    __builtin_amdgcn_sched_barrier(0);
+    read_tr(0, dtf0, qtf0);
+    sdp(r1, s1, dp1);
+    pds(s0, dp0, pw0, sw0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x400, 1, 0);  // exponential
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // other VALU
     }
+    // the phase's weights are complete here: without this use the compiler sinks their
+    // exponentials and packs next to their first use in the next phase
+    asm volatile("" ::"v"(pw0[0]), "v"(pw0[1]), "v"(sw0[0]), "v"(sw0[1]));
+    __builtin_amdgcn_sched_barrier(0);
+    read_tr(1, dtf1, qtf1);
+    dvdk(dtf0, qtf0, pw0, sw0);
+    pds(s1, dp1, pw1, sw1);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x400, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+    }
+    asm volatile("" ::"v"(pw1[0]), "v"(pw1[1]), "v"(sw1[0]), "v"(sw1[1]));
+    __builtin_amdgcn_sched_barrier(0);
+    dvdk(dtf1, qtf1, pw1, sw1);
   }
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
