@@ -42,9 +42,9 @@ PEAK_HBM_GBS = 8000.0
 # copy (profiles/attn_fwd_bf16_*_counters.md): (read bytes, written bytes).
 # Valid only for the kernel source the counters were taken on.
 PROFILED_TRAFFIC = {
-    "kernel_source_sha256": "cc19ac10dec27610f2f9d485e6d9fc85e3f5e1869750b040a6c5dd92e0e03885",
-    "vggt-518-s32": (1166.7e6, 90.0e6),
-    "omega-512-s64": (2930.7e6, 920.1e6),
+    "kernel_source_sha256": "55696b166e80aa9e64ed8a746d201adfd896f2adb8ddbb04ac594f94cfcbbb9d",
+    "vggt-518-s32": (1165.5e6, 90.0e6),
+    "omega-512-s64": (2930.3e6, 920.1e6),
 }
 
 
