@@ -226,7 +226,7 @@ void attn_fwd_bf16_kernel(AttnProblem p) {
   const u32x4* __restrict__ vtg = (const u32x4*)p.vt + (kseq * p.H + head) * p.ktiles_seq * 512;
   // or V in place: key j of this sequence at vg + j * vrow bytes
   const char* __restrict__ vg = (const char*)p.v + ((seq * p.k_seq_stride) * p.tok_stride + head * D) * 2;
-  const int vrow = (int)p.tok_stride * 2;  // at most 64 heads of 128 bytes
+  const int vrow = (int)p.tok_stride * 2;  // at most 128 heads of 128 bytes (host check)
 
   const int kbeg = split * p.keys_per_split;
   const int kend = min(nk_seq, kbeg + p.keys_per_split);
