@@ -74,6 +74,37 @@ def test_omega_variants_small(dtype, rope, norm):
         assert bool((go[:, Ta:] == SENTINEL).all()), "register rows of the output were written"
 
 
+def test_frame_ex_reads_no_register_rows():
+    # The register tokens (rows T_active .. T-1 of each frame) are outside every key set:
+    # with their K and V all NaN the active rows must still match the oracle.  Frame calls
+    # read V rows in place and stop at the last active key of each frame.
+    wl = workload.Workload("t", 53, S=3, gh=6, gw=11, n_special=4, patch_begin=0, H=2)
+    S, T, H, Ta = wl.S, wl.T, wl.H, 66  # 66 active keys: a full 64-key tile and 2 more
+    q, k, v = wl.qkv_bf16()
+    pos = wl.positions()
+    ref = oracle.frame_attn_ex(q, k, v, S, T, Ta, pos=pos)
+    k[:, Ta:] = 0x7FC0
+    v[:, Ta:] = 0x7FC0
+    fo = ffv.vggt_frame_attn_ex(to_dev(q), to_dev(k), to_dev(v), Ta, pos_yx=torch.from_numpy(pos).to(dev()))
+    check_bf16(to_f64(fo)[:, :Ta], ref, "frame_ex with NaN register rows")
+
+
+def test_global_ex_reads_no_register_rows():
+    # the same for the compacted global key set (active rows of every frame, then extras)
+    wl = workload.Workload("t", 54, S=3, gh=6, gw=11, n_special=4, patch_begin=0, H=2)
+    S, T, H, Ta, E = wl.S, wl.T, wl.H, 66, 2
+    q, k, v = wl.qkv_bf16()
+    xq, xk, xv = _extras(0xE78A, E, H, torch.bfloat16)
+    pos = wl.positions()
+    rf, rx = oracle.global_attn_ex(q, k, v, S, T, Ta, xq, xk, xv, pos=pos)
+    k[:, Ta:] = 0x7FC0
+    v[:, Ta:] = 0x7FC0
+    go, xo = ffv.vggt_global_attn_ex(to_dev(q), to_dev(k), to_dev(v), Ta, to_dev(xq), to_dev(xk), to_dev(xv),
+                                     pos_yx=torch.from_numpy(pos).to(dev()))
+    check_bf16(to_f64(go)[:, :Ta], rf, "global_ex frames with NaN register rows")
+    check_bf16(to_f64(xo), rx, "global_ex extras with NaN register rows")
+
+
 @pytest.mark.parametrize("splits", [1, 3])
 def test_global_ex_without_extras_matches_global(splits):
     # N = 3 * 149 = 447 keys: 7 key tiles, the last holding 63 keys

@@ -160,11 +160,27 @@ def test_frame_v_rows_stay_inside_the_frame(T):
     k = workload.normal_bf16(0xF1, (S, T, H, 64))
     v = workload.normal_bf16(0xF2, (S, T, H, 64))
     v[1] = 0x7FC0  # bf16 quiet NaN
-    out = to_f64(ffv.vggt_frame_attn(to_dev(q), to_dev(k), to_dev(v)))
+    with np.errstate(invalid="ignore"):  # frame 1's NaN outputs
+        out = to_f64(ffv.vggt_frame_attn(to_dev(q), to_dev(k), to_dev(v)))
     for s in (0, 2):
         ref = oracle.frame_attn(q[s:s + 1], k[s:s + 1], v[s:s + 1], 1, T)
         check_bf16(out[s:s + 1], ref, f"frame {s} beside a NaN frame, T={T}")
     assert np.isnan(out[1]).all()
+
+
+def test_many_heads():
+    # 128 heads (the most the library takes): a token row is 16 KiB, the stride the frame
+    # kernel uses when it reads V rows in place; global attention at N = 3 x 69 does too
+    S, T, H = 3, 69, 128
+    q = workload.normal_bf16(0xA0, (S, T, H, 64))
+    k = workload.normal_bf16(0xA1, (S, T, H, 64))
+    v = workload.normal_bf16(0xA2, (S, T, H, 64))
+    pos = workload.positions(T, 8, 8, 5)
+    qd, kd, vd, pd = to_dev(q), to_dev(k), to_dev(v), torch.from_numpy(pos).to(dev())
+    check_bf16(to_f64(ffv.vggt_frame_attn(qd, kd, vd, pos_yx=pd)), oracle.frame_attn(q, k, v, S, T, pos=pos),
+               "frame H=128")
+    check_bf16(to_f64(ffv.vggt_global_attn(qd, kd, vd, pos_yx=pd, kv_splits=2)),
+               oracle.global_attn(q, k, v, S, T, pos=pos), "global H=128 splits=2")
 
 
 def test_single_token_frames_return_values():
