@@ -692,3 +692,44 @@ def test_bf16_bars_see_a_lost_key_tile_at_full_size():
     assert not checks.bf16_ok(e_lost), e_lost  # ... the scale-aware bars reject it
     assert e_lost["nrmse"] > 2 * checks.BF16_NRMSE, e_lost
     assert checks.bf16_ok(e_full) and e_full["nrmse"] < 0.2 * checks.BF16_NRMSE, e_full
+
+
+def test_bf16_bars_sit_between_input_noise_and_plausible_bugs():
+    """Noise-floor calibration on global attention at 4 frames of 224x224 (N = 1044, RoPE
+    base 100), every row: the exact result rounded to bf16 and the result of inputs with one
+    element moved by one bf16 ulp pass the bars with room to spare; a kernel that forgot
+    the log2(e) factor of its exp2 scores, one that scaled by 1/d instead of 1/sqrt(d), and
+    ones that left a single rotation pair unrotated (highest row frequency, highest column
+    frequency, lowest row frequency) all fail them."""
+    import checks
+
+    wl = workload.WORKLOADS["vggt-224-s4"]
+    q, k, v = wl.qkv_bf16()
+    S, T, H, N = wl.S, wl.T, wl.H, wl.N
+    pos_grid = wl.positions()
+    pos = np.tile(pos_grid, (S, 1))
+    ref = oracle.global_attn(q, k, v, S, T, pos=pos_grid)
+
+    def as_bf16(x):
+        return oracle.to_f64(workload.f32_to_bf16_bits(x.astype(np.float32))).reshape(x.shape)
+
+    e_floor = checks.bf16_errors(as_bf16(ref), ref)
+    assert checks.bf16_ok(e_floor) and e_floor["nrmse"] < 0.2 * checks.BF16_NRMSE, e_floor
+    q1 = q.copy()
+    q1[0, 7, 0, 5] += 1  # one bf16 ulp on one element
+    e_ulp = checks.bf16_errors(as_bf16(oracle.global_attn(q1, k, v, S, T, pos=pos_grid)), ref)
+    assert checks.bf16_ok(e_ulp) and e_ulp["nrmse"] < 0.2 * checks.BF16_NRMSE, e_ulp
+
+    for scale in (0.125 / np.log2(np.e), 1.0 / 64):
+        e = checks.bf16_errors(as_bf16(oracle.global_attn(q, k, v, S, T, pos=pos_grid, scale=scale)), ref)
+        assert not checks.bf16_ok(e), (scale, e)
+
+    qf, kf = oracle.to_f64(q).reshape(N, H, 64), oracle.to_f64(k).reshape(N, H, 64)
+    qr, kr = oracle.rope(q.reshape(N, H, 64), pos, 100.0), oracle.rope(k.reshape(N, H, 64), pos, 100.0)
+    vf = oracle.to_f64(v).reshape(N, H, 64)
+    for d in (2, 34, 30):
+        q2, k2 = qr.copy(), kr.copy()
+        q2[..., d:d + 2] = qf[..., d:d + 2]
+        k2[..., d:d + 2] = kf[..., d:d + 2]
+        e = checks.bf16_errors(as_bf16(oracle.attention(q2, k2, vf)), ref.reshape(N, H, 64))
+        assert not checks.bf16_ok(e), (d, e)
