@@ -168,6 +168,24 @@ def test_frame_v_rows_stay_inside_the_frame(T):
     assert np.isnan(out[1]).all()
 
 
+def test_long_frames_take_vt_tiles():
+    # Frames of 8229 tokens have 33 query tiles per key set, so frame attention builds V^T
+    # tiles per frame instead of reading V in place (7900 tokens: 31 tiles, V in place);
+    # sampled rows against the oracle, RoPE on a 90 x 91 grid plus 39 special tokens
+    H = 2
+    for S, T in ((2, 8229), (2, 7900)):
+        gh, gw = 90, (T - 39) // 90
+        pos = workload.positions(T, gh, gw, T - gh * gw)
+        q = workload.normal_bf16(0xB0 + T, (S, T, H, 64))
+        k = workload.normal_bf16(0xB1 + T, (S, T, H, 64))
+        v = workload.normal_bf16(0xB2 + T, (S, T, H, 64))
+        out = ffv.vggt_frame_attn(to_dev(q), to_dev(k), to_dev(v), pos_yx=torch.from_numpy(pos).to(dev()))
+        rows = sample_rows(S * T, T, S, seed=T, n_random=64)
+        ref = oracle.frame_attn(q, k, v, S, T, pos=pos, rows=rows)
+        got = to_f64(out).reshape(S * T, H, 64)[rows]
+        check_bf16(got, ref, f"frame S={S} T={T} ({rows.size} rows)")
+
+
 def test_many_heads():
     # 128 heads (the most the library takes): a token row is 16 KiB, the stride the frame
     # kernel uses when it reads V rows in place; global attention at N = 3 x 69 does too
