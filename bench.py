@@ -92,6 +92,7 @@ def main() -> int:
     ap.add_argument("--no-backward", action="store_true", help="skip the attention-gradient measurement")
     ap.add_argument("--no-extras", action="store_true",
                     help="time only the headline step (no Q/K-norm, streaming or Omega sections)")
+    ap.add_argument("--no-power", action="store_true", help="skip the socket power / clock sampling")
     ap.add_argument("--cpu-row-stride", type=int, default=48)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (hardware-counter calibration)")
@@ -250,6 +251,8 @@ def main() -> int:
         "input_sha256": {name: hashlib.sha256(a.tobytes()).hexdigest() for name, a in (("q", q), ("k", k), ("v", v))},
     }
 
+    if not args.no_power:
+        result["power"] = bench_power(ffv, qd, kd, vd, posd, ws_g, flops["global"])
     if not args.no_extras:
         result["qknorm"] = bench_qknorm(ffv, qd, kd, vd, posd, ws_g, ws_f, max(3, args.steps // 2), flops)
     if not args.no_extras:
@@ -475,6 +478,84 @@ def bench_backward(ffv, qd, kd, vd, posd, iters, flops):
         "dkdv_kernel_ms": round(dkdv_ms, 4),
         "kernels_tflops": round(bwd_flops / ((dq_ms + dkdv_ms) * 1e-3) / 1e12, 2),
         "kernels_frac_of_bf16_peak": round(bwd_flops / ((dq_ms + dkdv_ms) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+    }
+
+
+def _smi_sample():
+    """One `amd-smi metric -p -c` reading: (socket power W, mean gfx clock MHz over the XCDs), or None."""
+    import subprocess
+
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-p", "-c", "--json"], capture_output=True, text=True, timeout=5)
+        if r.returncode != 0:
+            return None
+        d = json.loads(r.stdout)
+        g = d["gpu_data"][0] if isinstance(d, dict) else d[0]
+        clk = [v["clk"]["value"] for k, v in g["clock"].items()
+               if k.startswith("gfx_") and isinstance(v.get("clk"), dict)]
+        return float(g["power"]["socket_power"]["value"]), float(sum(clk) / len(clk))
+    except Exception:  # tool missing or output format differs: no sample
+        return None
+
+
+def bench_power(ffv, qd, kd, vd, posd, ws_g, flop, seconds=2.5, settle=0.8):
+    """Socket power and shader clock under sustained global attention.  The global call
+    runs back to back for `seconds` while a thread reads `amd-smi metric -p -c` every
+    0.1 s (after `settle` seconds, so the reading reflects the steady state); the
+    kernel times of the same window come from the library's kernel timer.  From these:
+    clock cycles per launch (mean kernel time x mean clock) and energy per launch
+    (mean socket power x mean call time)."""
+    import threading
+
+    import torch
+
+    if _smi_sample() is None:
+        return None
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        t0 = time.perf_counter()
+        while not stop.is_set():
+            if time.perf_counter() - t0 >= settle:
+                s = _smi_sample()
+                if s is not None:
+                    samples.append(s)
+            stop.wait(0.1)
+
+    go = torch.empty_like(qd)
+    ffv.vggt_global_attn(qd, kd, vd, out=go, pos_yx=posd, rope_base=100.0, kv_splits=0, workspace=ws_g)
+    torch.cuda.synchronize()
+    th = threading.Thread(target=sampler)
+    ffv.vggt_timer_start(4096)
+    t0 = time.perf_counter()
+    th.start()
+    n = 0
+    while time.perf_counter() - t0 < seconds and n < 4000:
+        for _ in range(8):
+            ffv.vggt_global_attn(qd, kd, vd, out=go, pos_yx=posd, rope_base=100.0, kv_splits=0, workspace=ws_g)
+        torch.cuda.synchronize()
+        n += 8
+    wall = time.perf_counter() - t0
+    stop.set()
+    th.join()
+    kern = [ms for kind, ms in ffv.vggt_timer_stop() if kind == "global"]
+    if not samples:
+        return None
+    watts = float(np.mean([s[0] for s in samples]))
+    mhz = float(np.mean([s[1] for s in samples]))
+    kms = float(np.mean(kern))
+    call_ms = wall * 1e3 / n
+    return {
+        "what": "global attention (S=32 workload) back to back; amd-smi socket power and gfx clock, "
+                "mean of the readings after the first %.1f s" % settle,
+        "calls": n, "samples": len(samples),
+        "socket_power_w": round(watts, 1),
+        "gfx_clock_mhz": round(mhz),
+        "kernel_ms": round(kms, 4),
+        "kernel_frac_of_bf16_peak": round(flop / (kms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "frac_of_peak_at_this_clock": round(flop / (kms * 1e-3) / 1e12 / (PEAK_BF16_TFLOPS * mhz / 2400.0), 4),
+        "mcycles_per_launch": round(kms * 1e-3 * mhz * 1e6 / 1e6, 3),
+        "joules_per_launch": round(watts * call_ms * 1e-3, 3),
     }
 
 
