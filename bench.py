@@ -259,6 +259,8 @@ def main() -> int:
         result["configs"] = bench_configs(ffv, dev, max(3, args.steps // 2), qd)
     if not (args.no_stream or args.no_extras):
         result["stream"] = bench_stream(ffv, dev, max(3, args.steps // 2), 2)
+    if not args.no_extras:
+        result["shard"] = bench_shard(ffv, qd, kd, vd, posd, max(5, args.steps // 2), flops["global"])
     if not (args.no_backward or args.no_extras):
         result["backward"] = bench_backward(ffv, qd, kd, vd, posd, max(3, args.steps // 4), flops)
     if not (args.no_omega or args.no_extras):
@@ -479,6 +481,73 @@ def bench_backward(ffv, qd, kd, vd, posd, iters, flops):
         "kernels_tflops": round(bwd_flops / ((dq_ms + dkdv_ms) * 1e-3) / 1e12, 2),
         "kernels_frac_of_bf16_peak": round(bwd_flops / ((dq_ms + dkdv_ms) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
     }
+
+
+def bench_shard(ffv, qd, kd, vd, posd, iters, flop_global, gpus=8, link_tbs=7 * 0.153):
+    """One GPU's share of global attention on an 8-GPU node, at its real shape (nothing here
+    uses a second GPU): (i) head-parallel, 16/8 = 2 heads of the whole 43968-token sequence
+    (after an all-to-all from token shards to head shards); (ii) query-parallel, the queries
+    of 32/8 = 4 frames against all keys (after an all-gather of K and V), run as the
+    cross-attention launch with the 32 frames' rotated keys viewed as 4 groups of 10992.  RoPE
+    is applied to that Q shard and to K before timing (the key owners rotate once per
+    layer).  The exchange times are a model: bytes per GPU over 7 xGMI links of 153 GB/s,
+    not measured."""
+    import torch
+
+    S, T, H = qd.shape[0], qd.shape[1], qd.shape[2]
+    N = S * T
+    out = {"gpus_modelled": gpus, "note": "kernels measured on one GPU at one GPU's share; exchange times modelled"}
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, kind):
+        fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+        ffv.vggt_timer_start(4 * iters)
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        kern = [ms for k, ms in ffv.vggt_timer_stop() if k == kind]
+        return float(np.median([a.elapsed_time(b) for a, b in ev])), float(np.mean(kern))
+
+    hs = H // gpus
+    if hs >= 1 and H % gpus == 0:
+        hq, hk, hv = (t[:, :, :hs].contiguous() for t in (qd, kd, vd))
+        ho = torch.empty_like(hq)
+        call, kern = timed(lambda: ffv.vggt_global_attn(hq, hk, hv, out=ho, pos_yx=posd, rope_base=100.0), "global")
+        fl = flop_global * hs / H
+        # sent per GPU: (gpus-1)/gpus of its token shard of Q, K and V, and of O on the way back
+        xbytes = 4 * (N // gpus) * H * 64 * 2 * (gpus - 1) / gpus
+        out["head_parallel"] = {
+            "shape": f"[{S}, {T}, {hs}, 64] per GPU, N={N}", "tflop": round(fl / 1e12, 4),
+            "call_ms": round(call, 4), "kernel_ms": round(kern, 4),
+            "kernel_frac_of_bf16_peak": round(fl / (kern * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "exchange_mb_per_gpu": round(xbytes / 1e6, 1),
+            "exchange_ms_model": round(xbytes / (link_tbs * 1e12) * 1e3, 4),
+        }
+    sq = S // gpus
+    if sq >= 1 and S % gpus == 0:
+        qs = qd[:sq].clone()
+        ffv.vggt_attn_rope(qs, posd, rope_base=100.0)
+        kr = kd.clone()
+        ffv.vggt_attn_rope(kr, posd, rope_base=100.0)
+        Dn = N // sq
+        kv, vv = kr.view(sq, Dn, H, 64), vd.view(sq, Dn, H, 64)
+        qo = torch.empty_like(qs)
+        call, kern = timed(lambda: ffv.vggt_descriptor_xattn(qs, kv, vv, out=qo), "xattn")
+        fl = flop_global / gpus
+        # received per GPU: the other shards of K and V
+        xbytes = 2 * N * H * 64 * 2 * (gpus - 1) / gpus
+        out["query_parallel"] = {
+            "shape": f"{sq * T} queries x {N} keys, H={H} per GPU", "tflop": round(fl / 1e12, 4),
+            "call_ms": round(call, 4), "kernel_ms": round(kern, 4),
+            "kernel_frac_of_bf16_peak": round(fl / (kern * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "exchange_mb_per_gpu": round(xbytes / 1e6, 1),
+            "exchange_ms_model": round(xbytes / (link_tbs * 1e12) * 1e3, 4),
+        }
+    return out
 
 
 def _smi_sample():
