@@ -93,8 +93,8 @@ __device__ __forceinline__ void store4(uint16_t* dst, const float* x, const f32x
 // ---------------------------------------------------------------------------
 
 struct SmemDq {
-  u32x4 k[2][64][8];   // K rows (also read transposed: the A operand of dQ^T += K^T dS^T)
-  u32x4 v[2][64][8];   // V rows
+  u32x4 k[3][64][8];   // K rows (also read transposed: the A operand of dQ^T += K^T dS^T)
+  u32x4 v[3][64][8];   // V rows
 };
 
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -169,17 +169,12 @@ void attn_bwd_dq_kernel(AttnBwdProblem p) {
   for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
     for (int db = 0; db < 4; ++db) acc[qb][db] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  for (int t = 0; t < p.ntile; ++t) {
-    const int stage = t & 1;
-    if (t + 1 < p.ntile) {
-      tile_barrier();  // every wave is done with the stage tile t+1 goes to
-      issue(stage ^ 1, t + 1);
-      wait_vmcnt<4>();  // tile t has landed (tile t+1 may still be in flight)
-    } else {
-      wait_vmcnt<0>();
-    }
-    tile_barrier();  // ... in every wave's copies
-    bf16x8 kf[4][2], vf[4][2], ktf[2][4];
+  // Three-slot ring, one barrier per tile.  Tile t+2 is issued in the middle of tile t, after the
+  // barrier that shows tile t+1 landed in every wave; its slot held tile t-1, whose reads every
+  // wave completed in tile t-1.  The K and V fragments of tile t+1 are read at that point too,
+  // into the registers tile t's fragments leave free after its last S/dP product.
+  bf16x8 kf[4][2], vf[4][2];
+  auto read_kv = [&](int stage) {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       const int row = 16 * kb + l16;
@@ -190,6 +185,15 @@ void attn_bwd_dq_kernel(AttnBwdProblem p) {
         vf[kb][dc] = as_bf16x8(sm.v[stage][row][slot]);
       }
     }
+  };
+  issue(1, min(1, p.ntile - 1));
+  wait_vmcnt<4>();  // tile 0 has landed (tile 1 may still be in flight) ...
+  tile_barrier();   // ... in every wave's copies
+  read_kv(0);
+  int stage = 0;  // ring slot of tile t
+  for (int t = 0; t < p.ntile; ++t) {
+    const int next = stage == 2 ? 0 : stage + 1;
+    bf16x8 ktf[2][4];
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
@@ -258,6 +262,18 @@ void attn_bwd_dq_kernel(AttnBwdProblem p) {
     // phase, and the hints above find no VALU work to place beside the MFMAs
     asm volatile("" ::"v"(w0[0]), "v"(w0[1]));
     __builtin_amdgcn_sched_barrier(0);
+    {
+      // past the last tile the copies repeat the last tile into free slots and the
+      // fragments read from them go unused, so the loop body has no branch here
+      wait_vmcnt<0>();  // tile t+1 has landed in this wave's copies ...
+      // the K^T reads of tile t have returned long ago; a counted wait the compiler sees lets
+      // the dQ products below go without waiting for the K and V reads issued next
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      tile_barrier();   // ... and in every wave's; every wave is done with tile t-1's slot
+      issue(next == 2 ? 0 : next + 1, min(t + 2, p.ntile - 1));
+      read_kv(next);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     mask(1);
     dq(0, w0);
     w1[0] = dsw(1, 0);
@@ -271,7 +287,9 @@ void attn_bwd_dq_kernel(AttnBwdProblem p) {
     asm volatile("" ::"v"(w1[0]), "v"(w1[1]));
     __builtin_amdgcn_sched_barrier(0);
     dq(1, w1);
+    stage = next;
   }
+  wait_vmcnt<0>();  // no copy may still be writing LDS when the workgroup ends
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int qi = qw + 16 * qb + l16;
