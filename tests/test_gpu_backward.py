@@ -82,15 +82,19 @@ def test_backward_small_full(dtype, rope, glob):
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("glob", [True, False])
-@pytest.mark.parametrize("shape", ["one_tile", "whole_tiles"])
+@pytest.mark.parametrize("shape", ["one_tile", "whole_tiles", "four_tiles"])
 def test_backward_tile_edges(dtype, glob, shape):
     """Key and query ranges at tile edges: one frame of 7 x 7 patches + 5 special tokens
-    (54 rows: a single ragged tile, the first tile also the last), and frames of 8 x 8
-    patches with no special tokens (64 rows: whole tiles, nothing masked)."""
+    (54 rows: a single ragged tile, the first tile also the last), frames of 8 x 8
+    patches with no special tokens (64 rows: whole tiles, nothing masked), and frames of
+    15 x 15 patches + 5 special tokens (230 rows: four key tiles per frame, eight for the
+    pair, the last ragged, so the tile ring wraps and its last copies repeat the last tile)."""
     if shape == "one_tile":
         wl = workload.Workload("t", 81, S=1, gh=7, gw=7, n_special=5, patch_begin=5, H=2)
-    else:
+    elif shape == "whole_tiles":
         wl = workload.Workload("t", 82, S=2, gh=8, gw=8, n_special=0, patch_begin=0, H=2)
+    else:
+        wl = workload.Workload("t", 83, S=2, gh=15, gw=15, n_special=5, patch_begin=5, H=2)
     S, T, H = wl.S, wl.T, wl.H
     q, k, v = wl.qkv_bf16() if dtype == torch.bfloat16 else wl.qkv_f32()
     g = _dout(0xD0D1, (S, T, H, 64), dtype)
