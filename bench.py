@@ -188,9 +188,9 @@ def main() -> int:
     med = {c: float(np.median(x)) for c, x in per_call.items()}
 
     flops = {
-        "frame": attn_flops(T, T) * S,
-        "global": attn_flops(N, N),
-        "xattn": attn_flops(N, S * Dn),
+        "frame": attn_flops(T, T, H) * S,
+        "global": attn_flops(N, N, H),
+        "xattn": attn_flops(N, S * Dn, H),
     }
     step_flops = sum(flops.values())
     ms_per_step = elapsed * 1e3 / args.steps
@@ -252,7 +252,7 @@ def main() -> int:
     }
 
     if not args.no_power:
-        result["power"] = bench_power(ffv, qd, kd, vd, posd, ws_g, flops["global"])
+        result["power"] = bench_power(ffv, qd, kd, vd, posd, ws_g, flops["global"], S, T, H)
     if not args.no_extras:
         result["qknorm"] = bench_qknorm(ffv, qd, kd, vd, posd, ws_g, ws_f, max(3, args.steps // 2), flops)
     if not args.no_extras:
@@ -567,19 +567,16 @@ def _smi_sample():
         return None
 
 
-def bench_power(ffv, qd, kd, vd, posd, ws_g, flop, seconds=2.5, settle=0.8):
-    """Socket power and shader clock under sustained global attention.  The global call
-    runs back to back for `seconds` while a thread reads `amd-smi metric -p -c` every
-    0.1 s (after `settle` seconds, so the reading reflects the steady state); the
-    kernel times of the same window come from the library's kernel timer.  From these:
-    clock cycles per launch (mean kernel time x mean clock) and energy per launch
-    (mean socket power x mean call time)."""
+def _sustained_power(ffv, call, kinds, seconds, settle):
+    """Run `call` back to back for `seconds` while a thread reads `amd-smi metric -p -c`
+    every 0.1 s (after `settle` seconds, so the readings reflect the steady state).
+    Returns (calls, mean socket W, mean gfx MHz, number of readings, mean ms per call,
+    mean kernel ms per call summed over the timer kinds in `kinds`), or None without
+    readings."""
     import threading
 
     import torch
 
-    if _smi_sample() is None:
-        return None
     samples, stop = [], threading.Event()
 
     def sampler():
@@ -591,33 +588,49 @@ def bench_power(ffv, qd, kd, vd, posd, ws_g, flop, seconds=2.5, settle=0.8):
                     samples.append(s)
             stop.wait(0.1)
 
-    go = torch.empty_like(qd)
-    ffv.vggt_global_attn(qd, kd, vd, out=go, pos_yx=posd, rope_base=100.0, kv_splits=0, workspace=ws_g)
+    call()
     torch.cuda.synchronize()
     th = threading.Thread(target=sampler)
-    ffv.vggt_timer_start(4096)
+    ffv.vggt_timer_start(20000)  # kernel records: up to 10000 calls of at most two timed kernels
     t0 = time.perf_counter()
     th.start()
     n = 0
-    while time.perf_counter() - t0 < seconds and n < 4000:
+    while time.perf_counter() - t0 < seconds and n < 10000:
         for _ in range(8):
-            ffv.vggt_global_attn(qd, kd, vd, out=go, pos_yx=posd, rope_base=100.0, kv_splits=0, workspace=ws_g)
+            call()
         torch.cuda.synchronize()
         n += 8
     wall = time.perf_counter() - t0
     stop.set()
     th.join()
-    kern = [ms for kind, ms in ffv.vggt_timer_stop() if kind == "global"]
+    kern = sum(ms for kind, ms in ffv.vggt_timer_stop() if kind in kinds) / n
     if not samples:
         return None
-    watts = float(np.mean([s[0] for s in samples]))
-    mhz = float(np.mean([s[1] for s in samples]))
-    kms = float(np.mean(kern))
-    call_ms = wall * 1e3 / n
-    return {
+    return (n, float(np.mean([s[0] for s in samples])), float(np.mean([s[1] for s in samples])), len(samples),
+            wall * 1e3 / n, kern)
+
+
+def bench_power(ffv, qd, kd, vd, posd, ws_g, flop, S, T, H, seconds=2.5, settle=0.8):
+    """Socket power and shader clock under sustained global attention, frame attention and
+    the global-attention backward (each call back to back for `seconds`, amd-smi read
+    every 0.1 s after `settle` seconds).  Kernel times of the same window come from the
+    library's kernel timer.  From these: clock cycles per launch (mean kernel time x mean
+    clock), energy per call (mean socket power x mean call time) and per algorithmic flop."""
+    import torch
+
+    if _smi_sample() is None:
+        return None
+    go = torch.empty_like(qd)
+    r = _sustained_power(ffv, lambda: ffv.vggt_global_attn(qd, kd, vd, out=go, pos_yx=posd, rope_base=100.0,
+                                                            kv_splits=0, workspace=ws_g),
+                         ("global",), seconds, settle)
+    if r is None:
+        return None
+    n, watts, mhz, ns, call_ms, kms = r
+    out = {
         "what": "global attention (S=32 workload) back to back; amd-smi socket power and gfx clock, "
                 "mean of the readings after the first %.1f s" % settle,
-        "calls": n, "samples": len(samples),
+        "calls": n, "samples": ns,
         "socket_power_w": round(watts, 1),
         "gfx_clock_mhz": round(mhz),
         "kernel_ms": round(kms, 4),
@@ -625,7 +638,42 @@ def bench_power(ffv, qd, kd, vd, posd, ws_g, flop, seconds=2.5, settle=0.8):
         "frac_of_peak_at_this_clock": round(flop / (kms * 1e-3) / 1e12 / (PEAK_BF16_TFLOPS * mhz / 2400.0), 4),
         "mcycles_per_launch": round(kms * 1e-3 * mhz * 1e6 / 1e6, 3),
         "joules_per_launch": round(watts * call_ms * 1e-3, 3),
+        "pj_per_flop": round(watts * call_ms * 1e-3 / flop * 1e12, 3),
     }
+    # frame attention of the same tensors, and the global-attention backward
+    fo = torch.empty_like(qd)
+    ws_f = torch.empty(max(1, ffv.vggt_frame_attn_workspace(S, T, H, True)), dtype=torch.uint8, device=qd.device)
+    frame_flop = attn_flops(T, T, H) * S
+    r = _sustained_power(ffv, lambda: ffv.vggt_frame_attn(qd, kd, vd, out=fo, pos_yx=posd, rope_base=100.0,
+                                                           workspace=ws_f),
+                         ("frame",), seconds, settle)
+    if r is not None:
+        n, watts, mhz, ns, call_ms, kms = r
+        out["frame"] = {"calls": n, "samples": ns, "socket_power_w": round(watts, 1), "gfx_clock_mhz": round(mhz),
+                        "call_ms": round(call_ms, 4), "kernel_ms": round(kms, 4),
+                        "joules_per_call": round(watts * call_ms * 1e-3, 4),
+                        "pj_per_flop": round(watts * call_ms * 1e-3 / frame_flop * 1e12, 3)}
+    import workload
+
+    dout = torch.from_numpy(workload.normal_bf16(0xBAC4, tuple(qd.shape)).view(np.int16)).to(qd.device).view(
+        torch.bfloat16)
+    o, lse = ffv.vggt_global_attn_train(qd, kd, vd, pos_yx=posd)
+    grads = tuple(torch.empty_like(qd) for _ in range(3))
+    ws_b = torch.empty(max(1, int(ffv.lib().vggt_attn_backward_workspace(S, T, H, 1, 1, 0))), dtype=torch.uint8,
+                       device=qd.device)
+    bwd_flop = 2.5 * flop
+    r = _sustained_power(ffv, lambda: ffv.vggt_global_attn_backward(qd, kd, vd, o, dout, lse, pos_yx=posd,
+                                                                     workspace=ws_b, grads=grads),
+                         ("bwd_dq", "bwd_dkdv"), seconds, settle)
+    if r is not None:
+        n, watts, mhz, ns, call_ms, kms = r
+        out["backward"] = {"calls": n, "samples": ns, "socket_power_w": round(watts, 1),
+                           "gfx_clock_mhz": round(mhz), "call_ms": round(call_ms, 4),
+                           "kernels_ms": round(kms, 4),
+                           "joules_per_call": round(watts * call_ms * 1e-3, 3),
+                           "pj_per_flop": round(watts * call_ms * 1e-3 / bwd_flop * 1e12, 3),
+                           "pj_per_executed_flop": round(watts * call_ms * 1e-3 / (bwd_flop * 7 / 5) * 1e12, 3)}
+    return out
 
 
 def bench_omega(ffv, dev, iters):
